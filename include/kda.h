@@ -1,0 +1,165 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) Kimi Delta Attention (KDA) core.
+ *
+ * KDA is a gated delta rule with per-channel diagonal decay. For every
+ * (sequence, head) the recurrent state S (Dk x Dv, fp32) evolves per token t as
+ *
+ *     S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T,
+ *     o_t = S_t^T q_t,              alpha_t = exp(g_t)  (g_t <= 0, per key channel)
+ *
+ * Sources: the delta rule as one correction step on the L2 value-retrieval
+ * error and KDA's diagonal (per-channel) forgetting factor are described in the
+ * Kimi K3 report (xxquant, English and Chinese editions), "Methodology notes"
+ * (DeltaNet and Delta Rule; Kimi Delta Attention) and in the SemiAnalysis
+ * Kimi K3 digest, section 1 (KDA). The same pages describe the prefill as a
+ * chunked rewrite with two kernels -- tensor preparation (decayed queries and
+ * keys, an inverse "UT" transform, causal matrices) and a blockwise recurrence
+ * (pseudo-values, outputs, updated state) -- and the decode step as constant
+ * cost, about 7*D^2 FLOPs and 8*D^2 bytes of fp32 state traffic per head and
+ * token (report, "Key data").
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor argument is a DEVICE pointer owned by the caller; the
+ *     library never allocates, frees or retains memory. Scratch memory is
+ *     passed in through `workspace` (size from kda_prefill_workspace_size).
+ *   - All work is enqueued asynchronously on `stream` (0 = the null stream);
+ *     no entry point synchronises. Results are visible after the caller
+ *     synchronises the stream.
+ *   - Layouts are dense row-major (C order) with the last index contiguous:
+ *       q, k  [tokens, H, Dk]     v, o  [tokens, H, Dv]
+ *       g     [tokens, H, Dk]     beta  [tokens, H]
+ *       state [seqs, H, Dk, Dv]   (row i = key channel, column j = value channel)
+ *   - q, k, v are fp32 (KDA_F32) or bf16 (KDA_BF16, raw 16-bit patterns);
+ *     g, beta, states and o are always fp32.
+ *   - q and k are expected to be L2-normalised per (token, head) by the
+ *     caller; the library uses them as given and applies no attention scale.
+ *   - Tensor pointers must be 16-byte aligned; workspace 256-byte aligned.
+ *   - Arguments are validated on the host BEFORE any HIP call. On any error
+ *     nothing is enqueued and no output is touched, except KDA_ERR_HIP, which
+ *     reports a failed launch (outputs then undefined).
+ *   - Device-side preconditions that are documented but not checked (their
+ *     violation gives unspecified results, never an out-of-bounds access,
+ *     because sequence ranges are clamped to [0, total_tokens) on the device):
+ *     cu_seqlens non-decreasing with cu_seqlens[num_seqs] == total_tokens;
+ *     finite inputs; g <= 0; within a chunk of 64 tokens the decay summed over
+ *     any 16 consecutive tokens stays below about 11 nats per channel when
+ *     q/k/v are bf16 (fp16 operand range) and below about 80 nats for fp32.
+ *   - The library keeps no global state besides the loaded code object and
+ *     is reentrant; calls on different streams may run concurrently if they
+ *     write disjoint outputs and workspaces.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum kda_status {
+    KDA_OK = 0,
+    KDA_ERR_INVALID_ARG = 1,  /* NULL required pointer, bad size, misalignment  */
+    KDA_ERR_UNSUPPORTED = 2,  /* valid but not implemented (dims, chunk size)   */
+    KDA_ERR_WORKSPACE = 3,    /* workspace NULL or smaller than required        */
+    KDA_ERR_HIP = 4           /* a HIP launch or runtime call failed            */
+} kda_status_t;
+
+typedef enum kda_dtype {
+    KDA_F32 = 0,              /* q, k, v in fp32                                 */
+    KDA_BF16 = 1              /* q, k, v in bf16                                 */
+} kda_dtype_t;
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int kda_version(void);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *kda_status_string(kda_status_t status);
+
+/*
+ * Bytes of device workspace kda_prefill_chunked needs for these sizes.
+ * Returns 0 when the sizes are invalid or unsupported (the same checks as
+ * kda_prefill_chunked). The size depends only on the arguments, so one
+ * allocation can be reused for every call with the same or smaller sizes.
+ */
+size_t kda_prefill_workspace_size(int64_t total_tokens, int32_t num_seqs, int32_t H,
+                                  int32_t Dk, int32_t Dv, int32_t chunk_size,
+                                  kda_dtype_t in_dtype);
+
+/*
+ * Chunked KDA prefill over one or more packed sequences.
+ *
+ * Computes, for every sequence s, head h and token t of s, o_t = S_t^T q_t of
+ * the recurrence above, starting from initial_state[s, h] (zeros if NULL), and
+ * optionally the state after the last token (final_state) and after every
+ * ckpt_interval tokens of each sequence (ckpt_states).
+ *
+ *   q, k, v, in_dtype  inputs as in the layout conventions ([total_tokens, H, D])
+ *   g                  [total_tokens, H, Dk] fp32 log-decay (alpha = exp(g))
+ *   beta               [total_tokens, H] fp32 write strengths
+ *   cu_seqlens         device int32 [num_seqs + 1]: sequence s owns tokens
+ *                      cu_seqlens[s] .. cu_seqlens[s+1]-1; cu_seqlens[0] = 0.
+ *                      NULL means one sequence of total_tokens (num_seqs must
+ *                      be 1). Zero-length sequences are allowed: their final
+ *                      state equals their initial state.
+ *   num_seqs, total_tokens, H, Dk, Dv   sizes; Dk, Dv in {64, 128}
+ *   chunk_size         must be 64
+ *   initial_state      [num_seqs, H, Dk, Dv] fp32 or NULL (zeros)
+ *   final_state        [num_seqs, H, Dk, Dv] fp32 or NULL (not written)
+ *   ckpt_interval      0 = no checkpoints; otherwise a positive multiple of
+ *                      chunk_size. Checkpoint m (m = 1, 2, ...) of sequence s
+ *                      is the state after its first m*ckpt_interval tokens.
+ *   ckpt_states        [ckpt_rows, H, Dk, Dv] fp32; required iff
+ *                      ckpt_interval > 0. Row c = base_s + m - 1 holds
+ *                      checkpoint m of sequence s, base_s = sum over earlier
+ *                      sequences of floor(L / ckpt_interval).
+ *   ckpt_rows          rows available in ckpt_states (the caller knows the
+ *                      lengths; the library does not read them on the host).
+ *                      Checkpoints whose row would be >= ckpt_rows are not
+ *                      written.
+ *   o                  [total_tokens, H, Dv] fp32 output
+ *   workspace          device scratch of at least
+ *                      kda_prefill_workspace_size(...) bytes, 256-byte aligned;
+ *                      its contents need no initialisation and are garbage
+ *                      afterwards. It must not be shared by concurrent calls.
+ *   stream             HIP stream the kernels are enqueued on
+ *
+ * Returns KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_WORKSPACE
+ * (validated before any launch) or KDA_ERR_HIP (launch failure).
+ * total_tokens == 0 is valid: only final_state (= initial state) is written.
+ */
+kda_status_t kda_prefill_chunked(
+    const void *q, const void *k, const void *v, kda_dtype_t in_dtype,
+    const float *g, const float *beta, const int32_t *cu_seqlens,
+    int32_t num_seqs, int64_t total_tokens, int32_t H, int32_t Dk, int32_t Dv,
+    int32_t chunk_size, const float *initial_state, float *final_state,
+    int64_t ckpt_interval, float *ckpt_states, int64_t ckpt_rows, float *o,
+    void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * One KDA decode step for B independent sequences (one new token each).
+ *
+ * For each (b, h): S <- (I - beta k k^T) Diag(exp(g)) S + beta k v^T and
+ * o = S^T q with the UPDATED S. The state is read and written in place
+ * (one read and one write of every element).
+ *
+ *   q, k   [B, H, Dk] (in_dtype); v [B, H, Dv] (in_dtype)
+ *   g      [B, H, Dk] fp32;  beta [B, H] fp32
+ *   state  [B, H, Dk, Dv] fp32, updated in place; must not overlap inputs or o
+ *   o      [B, H, Dv] fp32
+ *   Dk, Dv in {64, 128}; B, H >= 1 (B == 0 is a valid no-op).
+ *
+ * Returns KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED or KDA_ERR_HIP.
+ */
+kda_status_t kda_decode_step(
+    const void *q, const void *k, const void *v, kda_dtype_t in_dtype,
+    const float *g, const float *beta, int32_t B, int32_t H, int32_t Dk, int32_t Dv,
+    float *state, float *o, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */

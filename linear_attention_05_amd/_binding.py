@@ -1,0 +1,85 @@
+"""ctypes binding of libkda.so (include/kda.h).
+
+Argument marshalling only: tensors are passed as raw device pointers and the
+current torch stream is passed as the HIP stream. Every step of the
+computation runs in the library's HIP kernels; there is no fallback path, so
+a missing or unloadable libkda.so raises immediately."""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libkda.so")
+
+KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_WORKSPACE, KDA_ERR_HIP = range(5)
+KDA_F32, KDA_BF16 = 0, 1
+
+# Every symbol include/kda.h declares.
+EXPORTS = ("kda_version", "kda_status_string", "kda_prefill_workspace_size",
+           "kda_prefill_chunked", "kda_decode_step")
+
+_lib = None
+
+
+class KdaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)}")
+
+
+def load():
+    """Load libkda.so (built in-tree by linear_attention_05_amd/build.py)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it with `python -m linear_attention_05_amd.build` "
+            "(the KDA core has no non-HIP implementation)")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    lib.kda_version.argtypes = []
+    lib.kda_version.restype = ctypes.c_int
+    lib.kda_status_string.argtypes = [ctypes.c_int]
+    lib.kda_status_string.restype = ctypes.c_char_p
+    lib.kda_prefill_workspace_size.argtypes = [I64, I32, I32, I32, I32, I32, ctypes.c_int]
+    lib.kda_prefill_workspace_size.restype = SZ
+    lib.kda_prefill_chunked.argtypes = [
+        P, P, P, ctypes.c_int, P, P, P, I32, I64, I32, I32, I32, I32, P, P, I64, P, I64, P, P,
+        SZ, P]
+    lib.kda_prefill_chunked.restype = ctypes.c_int
+    lib.kda_decode_step.argtypes = [P, P, P, ctypes.c_int, P, P, I32, I32, I32, I32, P, P, P]
+    lib.kda_decode_step.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().kda_status_string(int(status)).decode()
+
+
+def version() -> int:
+    return load().kda_version()
+
+
+def workspace_size(total_tokens, num_seqs, H, Dk, Dv, dtype_code, chunk_size=64) -> int:
+    return int(load().kda_prefill_workspace_size(int(total_tokens), int(num_seqs), int(H),
+                                                 int(Dk), int(Dv), int(chunk_size),
+                                                 int(dtype_code)))
+
+
+def prefill_raw(q, k, v, dtype_code, g, beta, cu_seqlens, num_seqs, total_tokens, H, Dk, Dv,
+                chunk_size, initial_state, final_state, ckpt_interval, ckpt_states, ckpt_rows, o,
+                workspace, workspace_bytes, stream) -> int:
+    """Direct call of kda_prefill_chunked with integer pointers; returns the status."""
+    return load().kda_prefill_chunked(q, k, v, dtype_code, g, beta, cu_seqlens, num_seqs,
+                                      total_tokens, H, Dk, Dv, chunk_size, initial_state,
+                                      final_state, ckpt_interval, ckpt_states, ckpt_rows, o,
+                                      workspace, workspace_bytes, stream)
+
+
+def decode_raw(q, k, v, dtype_code, g, beta, B, H, Dk, Dv, state, o, stream) -> int:
+    """Direct call of kda_decode_step with integer pointers; returns the status."""
+    return load().kda_decode_step(q, k, v, dtype_code, g, beta, B, H, Dk, Dv, state, o, stream)

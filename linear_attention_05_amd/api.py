@@ -1,0 +1,130 @@
+"""Torch-tensor front end of the KDA core library (same names as the C ABI).
+
+PyTorch supplies device memory and the stream; this module only checks
+tensor properties, allocates outputs the caller did not pass, and forwards raw
+pointers to libkda.so. All arithmetic happens in the library's HIP kernels."""
+
+from __future__ import annotations
+
+import torch
+
+from . import _binding as B
+
+CHUNK = 64
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return B.KDA_BF16
+    if t.dtype == torch.float32:
+        return B.KDA_F32
+    raise TypeError(f"q/k/v must be bfloat16 or float32, got {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _check(t, name, dtype=None, shape=None, device=None):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _stream(device):
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def kda_prefill_workspace_size(total_tokens, num_seqs, H, Dk, Dv, dtype=torch.bfloat16,
+                               chunk_size=CHUNK) -> int:
+    code = B.KDA_BF16 if dtype == torch.bfloat16 else B.KDA_F32
+    return B.workspace_size(total_tokens, num_seqs, H, Dk, Dv, code, chunk_size)
+
+
+def kda_prefill_chunked(q, k, v, g, beta, *, cu_seqlens=None, num_seqs=None,
+                        initial_state=None, output_final_state=True, final_state=None,
+                        ckpt_interval=0, num_checkpoints=None, ckpt_states=None, o=None,
+                        workspace=None):
+    """Chunked KDA prefill (see include/kda.h, kda_prefill_chunked).
+
+    q, k [N, H, Dk], v [N, H, Dv] (bf16 or fp32, one dtype); g [N, H, Dk] fp32;
+    beta [N, H] fp32; cu_seqlens int32 [S+1] on the GPU or None (one sequence).
+    With ckpt_interval > 0 the caller gives num_checkpoints (= sum_s
+    floor(L_s / ckpt_interval)) or a preallocated ckpt_states.
+    Returns (o, final_state or None, ckpt_states or None)."""
+    dev = q.device
+    N, H, Dk = q.shape
+    Dv = v.shape[-1]
+    code = _dtype_code(q)
+    if num_seqs is None:
+        num_seqs = 1 if cu_seqlens is None else cu_seqlens.numel() - 1
+    _check(q, "q", q.dtype, (N, H, Dk), dev)
+    _check(k, "k", q.dtype, (N, H, Dk), dev)
+    _check(v, "v", q.dtype, (N, H, Dv), dev)
+    _check(g, "g", torch.float32, (N, H, Dk), dev)
+    _check(beta, "beta", torch.float32, (N, H), dev)
+    _check(cu_seqlens, "cu_seqlens", torch.int32, (num_seqs + 1,), dev)
+    _check(initial_state, "initial_state", torch.float32, (num_seqs, H, Dk, Dv), dev)
+    if o is None:
+        o = torch.empty((N, H, Dv), dtype=torch.float32, device=dev)
+    _check(o, "o", torch.float32, (N, H, Dv), dev)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((num_seqs, H, Dk, Dv), dtype=torch.float32, device=dev)
+    _check(final_state, "final_state", torch.float32, (num_seqs, H, Dk, Dv), dev)
+    if ckpt_interval > 0 and ckpt_states is None:
+        if num_checkpoints is None:
+            raise ValueError("ckpt_interval > 0 needs num_checkpoints or ckpt_states")
+        ckpt_states = torch.empty((max(int(num_checkpoints), 0), H, Dk, Dv),
+                                  dtype=torch.float32, device=dev)
+    if ckpt_states is not None:
+        _check(ckpt_states, "ckpt_states", torch.float32, None, dev)
+    need = B.workspace_size(N, num_seqs, H, Dk, Dv, code, CHUNK)
+    if need == 0:
+        raise B.KdaError(B.KDA_ERR_UNSUPPORTED, "kda_prefill_workspace_size")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    _check(workspace, "workspace", torch.uint8, None, dev)
+    ck_ptr = _ptr(ckpt_states) if ckpt_interval > 0 else None
+    ck_rows = int(ckpt_states.shape[0]) if ckpt_interval > 0 else 0
+    if ckpt_interval > 0 and ckpt_states.numel() == 0:
+        # zero checkpoint rows: any aligned non-null pointer is never written
+        ck_ptr = workspace.data_ptr()
+    st = B.prefill_raw(_ptr(q), _ptr(k), _ptr(v), code, _ptr(g), _ptr(beta), _ptr(cu_seqlens),
+                       num_seqs, N, H, Dk, Dv, CHUNK, _ptr(initial_state), _ptr(final_state),
+                       int(ckpt_interval), ck_ptr, ck_rows, _ptr(o), _ptr(workspace),
+                       workspace.numel(), _stream(dev))
+    if st != B.KDA_OK:
+        raise B.KdaError(st, "kda_prefill_chunked")
+    return o, final_state, ckpt_states
+
+
+def kda_decode_step(q, k, v, g, beta, state, o=None):
+    """One decode step, state [B, H, Dk, Dv] fp32 updated in place (include/kda.h).
+    Returns o [B, H, Dv] fp32."""
+    dev = q.device
+    Bsz, H, Dk = q.shape
+    Dv = v.shape[-1]
+    code = _dtype_code(q)
+    _check(q, "q", q.dtype, (Bsz, H, Dk), dev)
+    _check(k, "k", q.dtype, (Bsz, H, Dk), dev)
+    _check(v, "v", q.dtype, (Bsz, H, Dv), dev)
+    _check(g, "g", torch.float32, (Bsz, H, Dk), dev)
+    _check(beta, "beta", torch.float32, (Bsz, H), dev)
+    _check(state, "state", torch.float32, (Bsz, H, Dk, Dv), dev)
+    if o is None:
+        o = torch.empty((Bsz, H, Dv), dtype=torch.float32, device=dev)
+    _check(o, "o", torch.float32, (Bsz, H, Dv), dev)
+    st = B.decode_raw(_ptr(q), _ptr(k), _ptr(v), code, _ptr(g), _ptr(beta), Bsz, H, Dk, Dv,
+                      _ptr(state), _ptr(o), _stream(dev))
+    if st != B.KDA_OK:
+        raise B.KdaError(st, "kda_decode_step")
+    return o

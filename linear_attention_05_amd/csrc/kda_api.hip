@@ -1,0 +1,119 @@
+// kda_api.hip -- the C ABI (include/kda.h): host-side validation, workspace
+// sizing and launch of the gfx950 kernels. No HIP call happens before every
+// argument has been validated.
+#include "kda.h"
+
+#include "kda_internal.h"
+
+namespace {
+
+constexpr int kVersion = 100;  // 0.1.0
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool supported_dim(int32_t d) { return d == 64 || d == 128; }
+
+bool valid_dtype(kda_dtype_t t) { return t == KDA_F32 || t == KDA_BF16; }
+
+// Shared size checks of the prefill entry points (sizes only, no pointers).
+kda_status_t check_prefill_sizes(int64_t total_tokens, int32_t num_seqs, int32_t H, int32_t Dk,
+                                 int32_t Dv, int32_t chunk_size, kda_dtype_t in_dtype) {
+    if (total_tokens < 0 || num_seqs < 1 || H < 1 || Dk < 1 || Dv < 1 || !valid_dtype(in_dtype))
+        return KDA_ERR_INVALID_ARG;
+    if (total_tokens > (int64_t)INT32_MAX || (int64_t)num_seqs * H > (int64_t)INT32_MAX / 16)
+        return KDA_ERR_UNSUPPORTED;
+    if (!supported_dim(Dk) || !supported_dim(Dv) || chunk_size != kda::kChunk)
+        return KDA_ERR_UNSUPPORTED;
+    return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kda_version(void) { return kVersion; }
+
+const char* kda_status_string(kda_status_t s) {
+    switch (s) {
+        case KDA_OK: return "KDA_OK";
+        case KDA_ERR_INVALID_ARG: return "KDA_ERR_INVALID_ARG: invalid argument";
+        case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED: unsupported size or option";
+        case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE: workspace missing or too small";
+        case KDA_ERR_HIP: return "KDA_ERR_HIP: HIP launch or runtime failure";
+    }
+    return "unknown kda_status_t";
+}
+
+size_t kda_prefill_workspace_size(int64_t total_tokens, int32_t num_seqs, int32_t H, int32_t Dk,
+                                  int32_t Dv, int32_t chunk_size, kda_dtype_t in_dtype) {
+    if (check_prefill_sizes(total_tokens, num_seqs, H, Dk, Dv, chunk_size, in_dtype) != KDA_OK)
+        return 0;
+    return kda::prefill_workspace_bytes(total_tokens, num_seqs, H, Dk, Dv, in_dtype == KDA_BF16);
+}
+
+kda_status_t kda_prefill_chunked(const void* q, const void* k, const void* v,
+                                 kda_dtype_t in_dtype, const float* g, const float* beta,
+                                 const int32_t* cu_seqlens, int32_t num_seqs,
+                                 int64_t total_tokens, int32_t H, int32_t Dk, int32_t Dv,
+                                 int32_t chunk_size, const float* initial_state,
+                                 float* final_state, int64_t ckpt_interval, float* ckpt_states,
+                                 int64_t ckpt_rows, float* o, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream) {
+    kda_status_t st = check_prefill_sizes(total_tokens, num_seqs, H, Dk, Dv, chunk_size, in_dtype);
+    if (st != KDA_OK) return st;
+    if (!cu_seqlens && num_seqs != 1) return KDA_ERR_INVALID_ARG;
+    if (total_tokens > 0 && (!q || !k || !v || !g || !beta || !o)) return KDA_ERR_INVALID_ARG;
+    if (ckpt_interval < 0) return KDA_ERR_INVALID_ARG;
+    if (ckpt_interval > 0 && (ckpt_interval % chunk_size != 0)) return KDA_ERR_UNSUPPORTED;
+    if (ckpt_interval > 0 && (!ckpt_states || ckpt_rows < 0)) return KDA_ERR_INVALID_ARG;
+    if (ckpt_interval == 0 && (ckpt_states || ckpt_rows != 0)) return KDA_ERR_INVALID_ARG;
+    const void* ptrs[] = {q, k, v, g, beta, cu_seqlens, initial_state, final_state, ckpt_states, o};
+    for (const void* p : ptrs)
+        if (p && !aligned(p, 16)) return KDA_ERR_INVALID_ARG;
+    const size_t need =
+        kda::prefill_workspace_bytes(total_tokens, num_seqs, H, Dk, Dv, in_dtype == KDA_BF16);
+    if (!workspace || workspace_bytes < need) return KDA_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return KDA_ERR_INVALID_ARG;
+
+    kda::PrefillArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.bf16 = in_dtype == KDA_BF16;
+    a.g = g;
+    a.beta = beta;
+    a.cu_seqlens = cu_seqlens;
+    a.num_seqs = num_seqs;
+    a.total_tokens = total_tokens;
+    a.H = H;
+    a.Dk = Dk;
+    a.Dv = Dv;
+    a.initial_state = initial_state;
+    a.final_state = final_state;
+    a.ckpt_interval = ckpt_interval;
+    a.ckpt_states = ckpt_states;
+    a.ckpt_rows = ckpt_rows;
+    a.o = o;
+    a.workspace = workspace;
+    a.workspace_bytes = workspace_bytes;
+    return kda::launch_prefill(a, stream) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status_t kda_decode_step(const void* q, const void* k, const void* v, kda_dtype_t in_dtype,
+                             const float* g, const float* beta, int32_t B, int32_t H, int32_t Dk,
+                             int32_t Dv, float* state, float* o, hipStream_t stream) {
+    if (B < 0 || H < 1 || Dk < 1 || Dv < 1 || !valid_dtype(in_dtype)) return KDA_ERR_INVALID_ARG;
+    if (!supported_dim(Dk) || !supported_dim(Dv)) return KDA_ERR_UNSUPPORTED;
+    if ((int64_t)B * H > (int64_t)INT32_MAX) return KDA_ERR_UNSUPPORTED;
+    if (B == 0) return KDA_OK;
+    if (!q || !k || !v || !g || !beta || !state || !o) return KDA_ERR_INVALID_ARG;
+    const void* ptrs[] = {q, k, v, g, beta, state, o};
+    for (const void* p : ptrs)
+        if (!aligned(p, 16)) return KDA_ERR_INVALID_ARG;
+    return kda::launch_decode(q, k, v, in_dtype == KDA_BF16, g, beta, B, H, Dk, Dv, state, o,
+                              stream) == hipSuccess
+               ? KDA_OK
+               : KDA_ERR_HIP;
+}
+
+}  // extern "C"

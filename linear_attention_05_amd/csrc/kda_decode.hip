@@ -1,0 +1,175 @@
+// kda_decode.hip -- single-token KDA decode step for gfx950.
+//
+// Per (batch row b, head h) the step is
+//     a = exp(g);  S' = Diag(a) S;  r = S'^T k;  p = S'^T q
+//     u = beta (v - r);  o = p + (k . q) u;  S <- S' + k u^T
+// which is S_t = (I - beta k k^T) Diag(alpha) S_{t-1} + beta k v^T and
+// o = S_t^T q written so that every state element is read once and written
+// once. The pages size this step at about 7*D^2 FLOPs against 8*D^2 bytes of
+// fp32 state traffic per head and token (Kimi K3 report, "Key data"): under
+// one FLOP per byte, so the kernel is built for HBM bandwidth, with no MFMA.
+//
+// Mapping: one 256-thread workgroup per (b, h). Thread t owns the 4 adjacent
+// value columns 4*(t % CG) .. +3 (CG = Dv/4) of the key rows
+// rg, rg + RG, rg + 2*RG, ... (rg = t / CG, RG = 256/CG): one wave reads
+// 64/CG whole adjacent rows per 16-byte-per-lane load, so each load
+// instruction moves 1 KiB of contiguous state. The decayed slab stays in
+// VGPRs between the reduction and the write-back; r, p and k.q are reduced
+// across row groups with lane shuffles and then across the 4 waves in LDS, in
+// a fixed order (bitwise reproducible).
+#include "kda_internal.h"
+
+namespace kda {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_to_f32(unsigned short b) {
+    return __uint_as_float(static_cast<unsigned>(b) << 16);
+}
+
+template <bool BF16>
+__device__ __forceinline__ float load_in(const void* p, int64_t i) {
+    if constexpr (BF16)
+        return bf16_to_f32(static_cast<const unsigned short*>(p)[i]);
+    else
+        return static_cast<const float*>(p)[i];
+}
+
+template <bool BF16>
+__device__ __forceinline__ f32x4 load_in4(const void* p, int64_t i) {
+    if constexpr (BF16) {
+        u16x4 b = *reinterpret_cast<const u16x4*>(static_cast<const unsigned short*>(p) + i);
+        return f32x4{bf16_to_f32(b.x), bf16_to_f32(b.y), bf16_to_f32(b.z), bf16_to_f32(b.w)};
+    } else {
+        return *reinterpret_cast<const f32x4*>(static_cast<const float*>(p) + i);
+    }
+}
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+
+template <int DK, int DV, bool BF16>
+__global__ __launch_bounds__(kThreads) void decode_kernel(
+    const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
+    const float* __restrict__ g, const float* __restrict__ beta, float* __restrict__ state,
+    float* __restrict__ o) {
+    constexpr int CG = DV / 4;           // column groups (threads per row)
+    constexpr int RG = kThreads / CG;    // row groups
+    constexpr int RPT = DK / RG;         // rows per thread
+    constexpr int RGW = 64 / CG;         // row groups per wave
+    static_assert(RPT * RG == DK && CG * 4 == DV && RGW >= 1, "bad decode tiling");
+
+    __shared__ float s_a[DK], s_k[DK], s_q[DK];
+    __shared__ f32x4 s_red[kWaves][CG][2];
+    __shared__ float s_kq[kWaves];
+
+    const int t = threadIdx.x;
+    const int cg = t % CG;
+    const int rg = t / CG;
+    const int lane = t & 63;
+    const int wave = t >> 6;
+    const int64_t pair = blockIdx.x;  // b * H + h
+    float* S = state + pair * (int64_t)(DK * DV);
+
+    // 1. stream the thread's state slab in (all loads in flight at once)
+    f32x4 s[RPT];
+#pragma unroll
+    for (int m = 0; m < RPT; ++m)
+        s[m] = __builtin_nontemporal_load(
+            reinterpret_cast<const f32x4*>(S + (int64_t)(rg + m * RG) * DV) + cg);
+
+    // 2. per-row vectors into LDS; per-column inputs straight to registers
+    for (int i = t; i < DK; i += kThreads) {
+        s_a[i] = __expf(g[pair * DK + i]);
+        s_k[i] = load_in<BF16>(k, pair * DK + i);
+        s_q[i] = load_in<BF16>(q, pair * DK + i);
+    }
+    const f32x4 vv = load_in4<BF16>(v, pair * DV + 4 * cg);
+    const float bt = beta[pair];
+    __syncthreads();
+
+    // 3. decay in registers; partial S'^T k, S'^T q and k.q over this thread's rows
+    f32x4 r = {0.f, 0.f, 0.f, 0.f}, p = {0.f, 0.f, 0.f, 0.f};
+    float kq = 0.f;
+#pragma unroll
+    for (int m = 0; m < RPT; ++m) {
+        const int i = rg + m * RG;
+        const float ai = s_a[i], ki = s_k[i], qi = s_q[i];
+        s[m] *= ai;
+        r += s[m] * ki;
+        p += s[m] * qi;
+        kq += ki * qi;
+    }
+
+    // 4. reduce over the row groups of this wave (lanes CG apart)
+#pragma unroll
+    for (int off = CG; off < 64; off <<= 1) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            r[e] += __shfl_xor(r[e], off);
+            p[e] += __shfl_xor(p[e], off);
+        }
+        kq += __shfl_xor(kq, off);
+    }
+    if (lane < CG) {
+        s_red[wave][lane][0] = r;
+        s_red[wave][lane][1] = p;
+    }
+    if (lane == 0) s_kq[wave] = kq;
+    __syncthreads();
+
+    // 5. across waves (fixed order), then the delta-rule correction u
+    f32x4 rr = s_red[0][cg][0], pp = s_red[0][cg][1];
+    float kqt = s_kq[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) {
+        rr += s_red[w][cg][0];
+        pp += s_red[w][cg][1];
+        kqt += s_kq[w];
+    }
+    // (every key row belongs to exactly one row group, so kqt = k . q)
+    const f32x4 u = bt * (vv - rr);
+    if (rg == 0) {
+        const f32x4 out = pp + kqt * u;
+        *reinterpret_cast<f32x4*>(o + pair * DV + 4 * cg) = out;
+    }
+
+    // 6. rank-1 write and stream the slab back out
+#pragma unroll
+    for (int m = 0; m < RPT; ++m) {
+        const int i = rg + m * RG;
+        const f32x4 nv = s[m] + s_k[i] * u;
+        __builtin_nontemporal_store(nv, reinterpret_cast<f32x4*>(S + (int64_t)i * DV) + cg);
+    }
+}
+
+template <int DK, int DV>
+hipError_t launch_dims(const void* q, const void* k, const void* v, bool bf16, const float* g,
+                       const float* beta, int B, int H, float* state, float* o,
+                       hipStream_t stream) {
+    const dim3 grid((unsigned)((int64_t)B * H)), block(kThreads);
+    if (bf16)
+        hipLaunchKernelGGL((decode_kernel<DK, DV, true>), grid, block, 0, stream, q, k, v, g,
+                           beta, state, o);
+    else
+        hipLaunchKernelGGL((decode_kernel<DK, DV, false>), grid, block, 0, stream, q, k, v, g,
+                           beta, state, o);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode(const void* q, const void* k, const void* v, bool bf16,
+                         const float* g, const float* beta, int B, int H, int Dk, int Dv,
+                         float* state, float* o, hipStream_t stream) {
+    if ((int64_t)B * H == 0) return hipSuccess;
+    if (Dk == 128 && Dv == 128) return launch_dims<128, 128>(q, k, v, bf16, g, beta, B, H, state, o, stream);
+    if (Dk == 128 && Dv == 64) return launch_dims<128, 64>(q, k, v, bf16, g, beta, B, H, state, o, stream);
+    if (Dk == 64 && Dv == 128) return launch_dims<64, 128>(q, k, v, bf16, g, beta, B, H, state, o, stream);
+    if (Dk == 64 && Dv == 64) return launch_dims<64, 64>(q, k, v, bf16, g, beta, B, H, state, o, stream);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace kda

@@ -1,0 +1,51 @@
+// kda_internal.h -- declarations shared by the library's translation units
+// (host launchers implemented next to their kernels). Not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kda {
+
+// ---- decode ---------------------------------------------------------------
+hipError_t launch_decode(const void* q, const void* k, const void* v, bool bf16,
+                         const float* g, const float* beta, int B, int H, int Dk, int Dv,
+                         float* state, float* o, hipStream_t stream);
+
+// ---- prefill --------------------------------------------------------------
+struct PrefillArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    bool bf16;
+    const float* g;
+    const float* beta;
+    const int32_t* cu_seqlens;  // may be null (one sequence)
+    int num_seqs;
+    int64_t total_tokens;
+    int H, Dk, Dv;
+    const float* initial_state;
+    float* final_state;
+    int64_t ckpt_interval;
+    float* ckpt_states;
+    int64_t ckpt_rows;
+    float* o;
+    void* workspace;
+    size_t workspace_bytes;
+};
+
+// Bytes of workspace the prefill path needs (0 if unsupported).
+size_t prefill_workspace_bytes(int64_t total_tokens, int num_seqs, int H, int Dk, int Dv,
+                               bool bf16);
+
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+
+// Upper bound on the number of 64-token chunks of a packed batch.
+inline int64_t max_chunks(int64_t total_tokens, int num_seqs) {
+    return total_tokens / 64 + num_seqs;
+}
+
+constexpr int kChunk = 64;
+
+}  // namespace kda

@@ -1,0 +1,118 @@
+"""CPU tests of the C ABI: the library loads, exports every symbol include/kda.h
+declares, sizes workspaces, and rejects invalid arguments before any HIP call
+(fake pointers are safe here because validation fails first)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from linear_attention_05_amd import _binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+OK, INV, UNS, WS = B.KDA_OK, B.KDA_ERR_INVALID_ARG, B.KDA_ERR_UNSUPPORTED, B.KDA_ERR_WORKSPACE
+A = 0x100000  # fake, 256-byte aligned "device" address (never dereferenced)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_exported_set():
+    assert declared_functions() == sorted(B.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = B.load()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings():
+    assert B.version() >= 100
+    for s in range(5):
+        assert B.status_string(s).startswith("KDA_")
+    assert "unknown" in B.status_string(99)
+
+
+def ws_size(N=8192, S=1, H=32, Dk=128, Dv=128, chunk=64, dt=B.KDA_BF16):
+    return B.workspace_size(N, S, H, Dk, Dv, dt, chunk)
+
+
+def test_workspace_size():
+    per_chunk_bf16 = (192 * 128 + 8192) * 2 + 4 * 128
+    assert per_chunk_bf16 == 66048
+    assert ws_size() == 256 + 32 * (8192 // 64 + 1) * per_chunk_bf16
+    per_chunk_f32 = (192 * 64 + 8192) * 4 + 4 * 64
+    assert ws_size(256, 1, 2, 64, 64, 64, B.KDA_F32) == 256 + 2 * 5 * per_chunk_f32
+    assert ws_size(Dk=96) == 0
+    assert ws_size(chunk=32) == 0
+    assert ws_size(N=-1) == 0
+    assert ws_size(S=0) == 0
+    assert ws_size(dt=7) == 0
+    assert ws_size(N=0, S=3) > 0
+
+
+def prefill(**kw):
+    a = dict(q=A, k=A, v=A, dt=B.KDA_BF16, g=A, beta=A, cu=None, S=1, N=256, H=2, Dk=128,
+             Dv=128, chunk=64, s0=None, sf=A, ci=0, ck=None, ckr=0, o=A, ws=A,
+             wsb=10 ** 12, stream=None)
+    a.update(kw)
+    return B.prefill_raw(a["q"], a["k"], a["v"], a["dt"], a["g"], a["beta"], a["cu"], a["S"],
+                         a["N"], a["H"], a["Dk"], a["Dv"], a["chunk"], a["s0"], a["sf"],
+                         a["ci"], a["ck"], a["ckr"], a["o"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), INV), (dict(k=None), INV), (dict(v=None), INV), (dict(g=None), INV),
+    (dict(beta=None), INV), (dict(o=None), INV),
+    (dict(N=-5), INV), (dict(H=0), INV), (dict(S=0), INV), (dict(dt=3), INV),
+    (dict(Dk=96), UNS), (dict(Dv=32), UNS), (dict(chunk=128), UNS), (dict(N=2 ** 31), UNS),
+    (dict(S=2), INV),                                  # several sequences need cu_seqlens
+    (dict(ci=-64), INV), (dict(ci=96), UNS),           # interval not a multiple of 64
+    (dict(ci=128), INV),                               # interval without a buffer
+    (dict(ci=128, ck=A, ckr=-1), INV),
+    (dict(ck=A), INV), (dict(ckr=3), INV),             # buffer without an interval
+    (dict(q=A + 8), INV), (dict(g=A + 4), INV), (dict(o=A + 2), INV), (dict(sf=A + 8), INV),
+    (dict(ws=None), WS), (dict(wsb=1000), WS), (dict(ws=A + 16), INV),
+])
+def test_prefill_validation(kw, status):
+    assert prefill(**kw) == status
+
+
+def test_prefill_workspace_exact_boundary():
+    need = ws_size(256, 1, 2, 128, 128)
+    assert prefill(wsb=need - 1) == WS
+
+
+def decode(**kw):
+    a = dict(q=A, k=A, v=A, dt=B.KDA_BF16, g=A, beta=A, B=4, H=2, Dk=128, Dv=128, st=A, o=A,
+             stream=None)
+    a.update(kw)
+    return B.decode_raw(a["q"], a["k"], a["v"], a["dt"], a["g"], a["beta"], a["B"], a["H"],
+                        a["Dk"], a["Dv"], a["st"], a["o"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), OK),                                   # no-op, nothing launched
+    (dict(B=-1), INV), (dict(H=0), INV), (dict(dt=2), INV),
+    (dict(Dk=32), UNS), (dict(Dv=256), UNS),
+    (dict(q=None), INV), (dict(st=None), INV), (dict(o=None), INV), (dict(beta=None), INV),
+    (dict(st=A + 4), INV), (dict(v=A + 2), INV),
+])
+def test_decode_validation(kw, status):
+    assert decode(**kw) == status
+
+
+def test_binding_refuses_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    import linear_attention_05_amd as K
+    x = torch.zeros(1, 1, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        K.kda_decode_step(x, x, x, torch.zeros(1, 1, 64), torch.zeros(1, 1),
+                          torch.zeros(1, 1, 64, 64))
