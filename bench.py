@@ -1,0 +1,254 @@
+#!/usr/bin/env python3
+"""Benchmark of the MI355X KDA core (one GPU).
+
+One step = one chunked prefill (prepare + scan) of the 8192-token workload
+(B=1, H=32, D_k=D_v=128, bf16 q/k/v, fp32 g/beta/state, random fp32 initial
+state), inputs resident in HBM. The same run also times the batched decode
+workload (B=512, H=32, D=128, 64 consecutive in-place steps over the 1 GiB
+fp32 state) and the fp64 CPU oracle on a bounded sample of the prefill.
+
+Prints ONE JSON line. Per-kernel durations come from HIP events recorded on
+the stream the kernels run on (torch's current stream, which the binding
+passes to the library)."""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PREFILL_WORKLOAD = 1
+DECODE_WORKLOAD = 4
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "linear_attention_05_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch measured with rocprofv3 counters (profiles/traffic.json),
+    or None when absent or taken on different kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    k = t.get("kernels", {}).get(kernel)
+    if not k:
+        return None
+    return k.get("fetch_bytes", 0) + k.get("write_bytes", 0)
+
+
+def dev(arr):
+    import numpy as np
+    import torch
+    if arr.dtype == np.uint16:
+        return torch.from_numpy(arr.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(arr).cuda()
+
+
+def bench_prefill(steps, warmup):
+    import torch
+    import linear_attention_05_amd as K
+    from linear_attention_05_amd import _binding as B
+    from linear_attention_05_amd import accounting as acc
+    from synth import make_workload
+
+    x = make_workload(PREFILL_WORKLOAD)
+    N, H, D = x.total_tokens, x.H, x.Dk
+    q, k, v, g, beta, s0 = (dev(a) for a in (x.q, x.k, x.v, x.g, x.beta, x.initial_state))
+    o = torch.empty(N, H, D, device="cuda")
+    fs = torch.empty(1, H, D, D, device="cuda")
+    ws = torch.empty(K.kda_prefill_workspace_size(N, 1, H, D, D), dtype=torch.uint8, device="cuda")
+
+    def phase(p):
+        K.kda_prefill_chunked(q, k, v, g, beta, initial_state=s0, final_state=fs, o=o,
+                              workspace=ws, phases=p)
+
+    for _ in range(warmup):
+        phase(B.PHASE_PREPARE)
+        phase(B.PHASE_SCAN)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record()
+        phase(B.PHASE_PREPARE)
+        ev[i][1].record()
+        phase(B.PHASE_SCAN)
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    k1_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
+    k2_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
+    n_chunks = (N + 63) // 64
+    flops = N * H * acc.prefill_flops_per_token_head(D, D)
+    return dict(
+        wall_ms=wall / steps * 1e3, k1_ms=k1_ms, k2_ms=k2_ms, n_tok=N, H=H, D=D, flops=flops,
+        compulsory_bytes=acc.prefill_compulsory_bytes(N, H, D, D, 2, 1, 1),
+        k1_bytes=acc.k1_bytes(N, H, D, 2, 2, n_chunks),
+        k2_bytes=acc.k2_bytes(N, H, D, D, 2, 2, n_chunks, 1, 1),
+        inputs=x)
+
+
+def bench_decode(steps, warmup):
+    import numpy as np
+    import torch
+    import linear_attention_05_amd as K
+    from linear_attention_05_amd import accounting as acc
+    from synth import WORKLOADS, decode_state, decode_step_inputs, workload_seed
+    from concurrent.futures import ThreadPoolExecutor
+
+    w = WORKLOADS[DECODE_WORKLOAD]
+    Bsz, H, D = w["B"], w["H"], w["D"]
+    seed = workload_seed(DECODE_WORKLOAD)
+    state = dev(decode_state(Bsz, H, D, D, seed))
+    with ThreadPoolExecutor(8) as ex:
+        host = list(ex.map(lambda t: decode_step_inputs(Bsz, H, D, D, w["dtype"], seed, t),
+                           range(steps)))
+    inp = [tuple(dev(a) for a in (s.q, s.k, s.v, s.g, s.beta)) for s in host]
+    o = torch.empty(Bsz, H, D, device="cuda")
+    for i in range(warmup):
+        K.kda_decode_step(*inp[i % steps], state, o)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record()
+        K.kda_decode_step(*inp[i], state, o)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [e[0].elapsed_time(e[1]) for e in ev]
+    kern_ms = float(np.median(per))
+    byts = Bsz * H * acc.decode_bytes_per_head_token(D, D, 2)
+    return dict(wall_ms=wall / steps * 1e3, kernel_ms=kern_ms, mean_ms=float(np.mean(per)),
+                bytes=byts, flops=Bsz * H * acc.decode_flops_per_head_token(D, D))
+
+
+def cpu_baseline(x, target_s=15.0):
+    """fp64 oracle on all 8192 tokens of a few heads (all value columns),
+    extrapolated to the whole workload's tokens/s."""
+    import numpy as np
+    from oracle import recurrence
+
+    cores = recurrence.num_threads(0)
+
+    def run(heads):
+        units = np.array([(0, h, cb) for h in heads for cb in range(x.Dv // 16)], np.int32)
+        t = time.perf_counter()
+        recurrence.prefill(x.q, x.k, x.v, x.g, x.beta, x.cu_seqlens, initial_state=x.initial_state,
+                           units=units, col_block=16)
+        return time.perf_counter() - t
+
+    t1 = run([0])
+    n = int(max(1, min(x.H, round(target_s / max(t1, 1e-3)))))
+    tn = run(list(range(n)))
+    per_head = tn / n
+    full = per_head * x.H
+    return dict(value=x.total_tokens / full / 1e6, unit="Mtok/s", cores=cores, kind="oracle",
+                sample=f"all {x.total_tokens} tokens x {n} of {x.H} heads x all {x.Dv} value "
+                       f"columns, fp64 token recurrence, {tn:.1f} s; scaled to {x.H} heads",
+                seconds=tn)
+
+
+def roofline(bytes_, ms, traffic=None):
+    gbps = bytes_ / (ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": round(gbps, 1), "peak": 8000.0, "unit": "GB/s",
+            "frac": round(gbps / 8000.0, 4), "traffic": traffic}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--decode-steps", type=int, default=64)
+    ap.add_argument("--only", choices=["all", "prefill", "decode"], default="all")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        if int(os.environ.get("RANK", "0")) == 0:
+            print(f"bench.py: this KDA core build runs on one GPU; --gpus {args.gpus} "
+                  f"(WORLD_SIZE={world}) is not supported. Independent (sequence, head) "
+                  "pairs would shard across GPUs without communication.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    import linear_attention_05_amd as K
+    K.load_library()
+
+    out = {}
+    if args.only in ("all", "prefill"):
+        p = bench_prefill(args.steps, args.warmup)
+        step_ms = p["wall_ms"]
+        mtok = p["n_tok"] / (step_ms * 1e-3) / 1e6
+        k1 = roofline(p["k1_bytes"], p["k1_ms"], measured_traffic("k1_prep"))
+        k2 = roofline(p["k2_bytes"], p["k2_ms"], measured_traffic("k2_scan"))
+        dominant, dom_name = (k2, "k2_scan") if p["k2_ms"] >= p["k1_ms"] else (k1, "k1_prep")
+        dominant = dict(dominant, kernel=dom_name)
+        out.update({
+            "metric": "KDA prefill Mtok/s & TFLOP/s (H=32,D=128); decode state HBM GB/s vs peak",
+            "value": round(mtok, 3), "unit": "Mtok/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(step_ms, 4), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16 in; f16 MFMA, f32 accum/state",
+            "data": "synthetic (seeded; q,k L2-normalised N(0,1); v N(0,1); g=-exp(N(-4,0.5)); "
+                    "beta=sigmoid(N(0,1)); S0 N(0,0.02))",
+            "config": {"workload": "KDA prefill B=1 T=8192 H=32 Dk=Dv=128 C=64 bf16, "
+                                   "fp32 initial+final state", "seq_len": p["n_tok"],
+                       "heads": p["H"], "head_dim": p["D"], "chunk": 64},
+            "roofline": dominant,
+            "prefill": {
+                "tflops_algorithmic": round(p["flops"] / (step_ms * 1e-3) / 1e12, 2),
+                "flops_per_step": p["flops"],
+                "path_compulsory_bytes": p["compulsory_bytes"],
+                "path_roofline_frac": round(p["compulsory_bytes"] / (step_ms * 1e-3) / 8e12, 4),
+                "k1_prep": dict(k1, ms=round(p["k1_ms"], 4), bytes=p["k1_bytes"]),
+                "k2_scan": dict(k2, ms=round(p["k2_ms"], 4), bytes=p["k2_bytes"]),
+            },
+        })
+    if args.only in ("all", "decode"):
+        d = bench_decode(args.decode_steps, min(args.warmup, args.decode_steps))
+        rd = roofline(d["bytes"], d["kernel_ms"], measured_traffic("decode"))
+        out["decode"] = dict(
+            workload="KDA decode B=512 H=32 D=128 bf16, fp32 state [512,32,128,128] in place",
+            steps=args.decode_steps, us_per_step=round(d["kernel_ms"] * 1e3, 2),
+            wall_us_per_step=round(d["wall_ms"] * 1e3, 2), state_bytes_per_step=d["bytes"],
+            gbps=rd["achieved"], frac_of_peak=rd["frac"], roofline=dict(rd, kernel="decode"))
+        if "metric" not in out:
+            out.update({"metric": "KDA decode state HBM GB/s", "value": rd["achieved"],
+                        "unit": "GB/s", "n_gpus": 1, "steps": args.decode_steps,
+                        "warmup": args.warmup, "ms_per_step": round(d["wall_ms"], 4),
+                        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+                        "dtype": "bf16 in; f32 state", "data": "synthetic",
+                        "config": {"workload": out["decode"]["workload"]},
+                        "roofline": out["decode"]["roofline"]})
+    if args.only in ("all", "prefill") and not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(p["inputs"])
+        out["cpu_baseline"]["seconds"] = round(out["cpu_baseline"]["seconds"], 2)
+        out["cpu_baseline"]["value"] = round(out["cpu_baseline"]["value"], 5)
+    out["kernel_source_sha"] = kernel_source_sha()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

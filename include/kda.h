@@ -138,6 +138,31 @@ kda_status_t kda_prefill_chunked(
     int64_t ckpt_interval, float *ckpt_states, int64_t ckpt_rows, float *o,
     void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Phases of the chunked prefill (bit mask for kda_prefill_chunked_phases). */
+#define KDA_PHASE_PREPARE 1u  /* chunk tensor preparation: writes the workspace   */
+#define KDA_PHASE_SCAN 2u     /* blockwise recurrence: reads the workspace, writes
+                                 o and the states                                 */
+
+/*
+ * kda_prefill_chunked split into its two phases. Same arguments and
+ * validation as kda_prefill_chunked, plus `phases`, a non-zero subset of
+ * KDA_PHASE_PREPARE | KDA_PHASE_SCAN (both = kda_prefill_chunked).
+ * PREPARE reads q, k, g, beta and cu_seqlens and fills the workspace; SCAN
+ * reads v, cu_seqlens, initial_state and that workspace and writes o,
+ * final_state and ckpt_states. A SCAN-only call must follow a PREPARE of the
+ * same inputs into the same workspace, ordered before it (same stream, or an
+ * event); the library does not check this. Lets a caller time the phases or
+ * overlap the preparation of one batch with the scan of another on a second
+ * stream (each batch with its own workspace).
+ */
+kda_status_t kda_prefill_chunked_phases(
+    const void *q, const void *k, const void *v, kda_dtype_t in_dtype,
+    const float *g, const float *beta, const int32_t *cu_seqlens,
+    int32_t num_seqs, int64_t total_tokens, int32_t H, int32_t Dk, int32_t Dv,
+    int32_t chunk_size, const float *initial_state, float *final_state,
+    int64_t ckpt_interval, float *ckpt_states, int64_t ckpt_rows, float *o,
+    void *workspace, size_t workspace_bytes, uint32_t phases, hipStream_t stream);
+
 /*
  * One KDA decode step for B independent sequences (one new token each).
  *

@@ -18,7 +18,8 @@ KDA_F32, KDA_BF16 = 0, 1
 
 # Every symbol include/kda.h declares.
 EXPORTS = ("kda_version", "kda_status_string", "kda_prefill_workspace_size",
-           "kda_prefill_chunked", "kda_decode_step")
+           "kda_prefill_chunked", "kda_prefill_chunked_phases", "kda_decode_step")
+PHASE_PREPARE, PHASE_SCAN = 1, 2
 
 _lib = None
 
@@ -50,6 +51,9 @@ def load():
         P, P, P, ctypes.c_int, P, P, P, I32, I64, I32, I32, I32, I32, P, P, I64, P, I64, P, P,
         SZ, P]
     lib.kda_prefill_chunked.restype = ctypes.c_int
+    lib.kda_prefill_chunked_phases.argtypes = list(lib.kda_prefill_chunked.argtypes[:-1]) + [
+        ctypes.c_uint32, P]
+    lib.kda_prefill_chunked_phases.restype = ctypes.c_int
     lib.kda_decode_step.argtypes = [P, P, P, ctypes.c_int, P, P, I32, I32, I32, I32, P, P, P]
     lib.kda_decode_step.restype = ctypes.c_int
     _lib = lib
@@ -78,6 +82,16 @@ def prefill_raw(q, k, v, dtype_code, g, beta, cu_seqlens, num_seqs, total_tokens
                                       total_tokens, H, Dk, Dv, chunk_size, initial_state,
                                       final_state, ckpt_interval, ckpt_states, ckpt_rows, o,
                                       workspace, workspace_bytes, stream)
+
+
+def prefill_phases_raw(q, k, v, dtype_code, g, beta, cu_seqlens, num_seqs, total_tokens, H, Dk,
+                       Dv, chunk_size, initial_state, final_state, ckpt_interval, ckpt_states,
+                       ckpt_rows, o, workspace, workspace_bytes, phases, stream) -> int:
+    """Direct call of kda_prefill_chunked_phases; returns the status."""
+    return load().kda_prefill_chunked_phases(q, k, v, dtype_code, g, beta, cu_seqlens, num_seqs,
+                                             total_tokens, H, Dk, Dv, chunk_size, initial_state,
+                                             final_state, ckpt_interval, ckpt_states, ckpt_rows,
+                                             o, workspace, workspace_bytes, phases, stream)
 
 
 def decode_raw(q, k, v, dtype_code, g, beta, B, H, Dk, Dv, state, o, stream) -> int:

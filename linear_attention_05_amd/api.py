@@ -53,13 +53,15 @@ def kda_prefill_workspace_size(total_tokens, num_seqs, H, Dk, Dv, dtype=torch.bf
 def kda_prefill_chunked(q, k, v, g, beta, *, cu_seqlens=None, num_seqs=None,
                         initial_state=None, output_final_state=True, final_state=None,
                         ckpt_interval=0, num_checkpoints=None, ckpt_states=None, o=None,
-                        workspace=None):
+                        workspace=None, phases=B.PHASE_PREPARE | B.PHASE_SCAN):
     """Chunked KDA prefill (see include/kda.h, kda_prefill_chunked).
 
     q, k [N, H, Dk], v [N, H, Dv] (bf16 or fp32, one dtype); g [N, H, Dk] fp32;
     beta [N, H] fp32; cu_seqlens int32 [S+1] on the GPU or None (one sequence).
     With ckpt_interval > 0 the caller gives num_checkpoints (= sum_s
     floor(L_s / ckpt_interval)) or a preallocated ckpt_states.
+    phases selects prepare (K1), scan (K2) or both (kda_prefill_chunked_phases);
+    a scan-only call must reuse the workspace of a preceding prepare.
     Returns (o, final_state or None, ckpt_states or None)."""
     dev = q.device
     N, H, Dk = q.shape
@@ -98,10 +100,11 @@ def kda_prefill_chunked(q, k, v, g, beta, *, cu_seqlens=None, num_seqs=None,
     if ckpt_interval > 0 and ckpt_states.numel() == 0:
         # zero checkpoint rows: any aligned non-null pointer is never written
         ck_ptr = workspace.data_ptr()
-    st = B.prefill_raw(_ptr(q), _ptr(k), _ptr(v), code, _ptr(g), _ptr(beta), _ptr(cu_seqlens),
-                       num_seqs, N, H, Dk, Dv, CHUNK, _ptr(initial_state), _ptr(final_state),
-                       int(ckpt_interval), ck_ptr, ck_rows, _ptr(o), _ptr(workspace),
-                       workspace.numel(), _stream(dev))
+    st = B.prefill_phases_raw(_ptr(q), _ptr(k), _ptr(v), code, _ptr(g), _ptr(beta),
+                              _ptr(cu_seqlens), num_seqs, N, H, Dk, Dv, CHUNK,
+                              _ptr(initial_state), _ptr(final_state), int(ckpt_interval), ck_ptr,
+                              ck_rows, _ptr(o), _ptr(workspace), workspace.numel(), int(phases),
+                              _stream(dev))
     if st != B.KDA_OK:
         raise B.KdaError(st, "kda_prefill_chunked")
     return o, final_state, ckpt_states

@@ -51,14 +51,17 @@ size_t kda_prefill_workspace_size(int64_t total_tokens, int32_t num_seqs, int32_
     return kda::prefill_workspace_bytes(total_tokens, num_seqs, H, Dk, Dv, in_dtype == KDA_BF16);
 }
 
-kda_status_t kda_prefill_chunked(const void* q, const void* k, const void* v,
-                                 kda_dtype_t in_dtype, const float* g, const float* beta,
-                                 const int32_t* cu_seqlens, int32_t num_seqs,
-                                 int64_t total_tokens, int32_t H, int32_t Dk, int32_t Dv,
-                                 int32_t chunk_size, const float* initial_state,
-                                 float* final_state, int64_t ckpt_interval, float* ckpt_states,
-                                 int64_t ckpt_rows, float* o, void* workspace, size_t workspace_bytes,
-                                 hipStream_t stream) {
+kda_status_t kda_prefill_chunked_phases(const void* q, const void* k, const void* v,
+                                        kda_dtype_t in_dtype, const float* g, const float* beta,
+                                        const int32_t* cu_seqlens, int32_t num_seqs,
+                                        int64_t total_tokens, int32_t H, int32_t Dk, int32_t Dv,
+                                        int32_t chunk_size, const float* initial_state,
+                                        float* final_state, int64_t ckpt_interval,
+                                        float* ckpt_states, int64_t ckpt_rows, float* o,
+                                        void* workspace, size_t workspace_bytes, uint32_t phases,
+                                        hipStream_t stream) {
+    if (phases == 0 || (phases & ~(KDA_PHASE_PREPARE | KDA_PHASE_SCAN)) != 0)
+        return KDA_ERR_INVALID_ARG;
     kda_status_t st = check_prefill_sizes(total_tokens, num_seqs, H, Dk, Dv, chunk_size, in_dtype);
     if (st != KDA_OK) return st;
     if (!cu_seqlens && num_seqs != 1) return KDA_ERR_INVALID_ARG;
@@ -96,7 +99,23 @@ kda_status_t kda_prefill_chunked(const void* q, const void* k, const void* v,
     a.o = o;
     a.workspace = workspace;
     a.workspace_bytes = workspace_bytes;
+    a.phases = phases;
     return kda::launch_prefill(a, stream) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status_t kda_prefill_chunked(const void* q, const void* k, const void* v,
+                                 kda_dtype_t in_dtype, const float* g, const float* beta,
+                                 const int32_t* cu_seqlens, int32_t num_seqs,
+                                 int64_t total_tokens, int32_t H, int32_t Dk, int32_t Dv,
+                                 int32_t chunk_size, const float* initial_state,
+                                 float* final_state, int64_t ckpt_interval, float* ckpt_states,
+                                 int64_t ckpt_rows, float* o, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
+    return kda_prefill_chunked_phases(q, k, v, in_dtype, g, beta, cu_seqlens, num_seqs,
+                                      total_tokens, H, Dk, Dv, chunk_size, initial_state,
+                                      final_state, ckpt_interval, ckpt_states, ckpt_rows, o,
+                                      workspace, workspace_bytes,
+                                      KDA_PHASE_PREPARE | KDA_PHASE_SCAN, stream);
 }
 
 kda_status_t kda_decode_step(const void* q, const void* k, const void* v, kda_dtype_t in_dtype,

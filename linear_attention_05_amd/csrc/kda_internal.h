@@ -33,6 +33,7 @@ struct PrefillArgs {
     float* o;
     void* workspace;
     size_t workspace_bytes;
+    unsigned phases;  // bit 0: prepare (prep + K1), bit 1: scan (K2)
 };
 
 // Bytes of workspace the prefill path needs (0 if unsupported).

@@ -59,6 +59,22 @@ __device__ __forceinline__ float bf16_to_f32(unsigned short b) {
     return __uint_as_float(static_cast<unsigned>(b) << 16);
 }
 
+// Sum of a value over lane pairs (l, l ^ 16) / (l, l ^ 32), with the two
+// addends in the same order in both lanes (v_permlane16/32_swap).
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float pair_sum16(float v) {
+    const u32x2 r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float pair_sum32(float v) {
+    const u32x2 r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// 2^x on the hardware exponential (inputs here are differences of decay
+// sums, far from the range where the library wrapper's rescaling matters).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // K-slab permutation: slot (q, e) -> index inside a 32-wide slab.
 __device__ __forceinline__ int perm32(int q, int e) {
     return e < 4 ? 4 * q + e : 16 + 4 * q + (e - 4);
@@ -235,6 +251,15 @@ __device__ __forceinline__ void locate_chunk(int ci, const int32_t* cu, const in
 }
 
 // ---------------------------------------------------------------- K1 -----
+// One workgroup per (chunk, head). Phases, separated by barriers:
+//   stage   K and g into LDS (16-byte loads), beta; cumulative sum of g per
+//           channel in fp64, stored as G*log2(e) in place of g
+//   A       the 10 lower 16x16 block pairs of A (to LDS) and of P (to the
+//           handoff); also the Qd, Kc^T and Gamma_last handoff
+//   inverse (I + A)^-1 by forward substitution, all four waves: wave w owns
+//           columns 16w..16w+15, four lanes share a column and split each
+//           row's inner sum, two lane exchanges combine them
+//   W       -W = -Ainv diag(beta) Kd via MFMA on W^T tiles; Ab = Ainv diag(beta)
 template <int DK, bool BF16>
 __global__ __launch_bounds__(kThreads) void k1_prep_kernel(
     const void* __restrict__ qin, const void* __restrict__ kin, const float* __restrict__ g,
@@ -254,9 +279,10 @@ __global__ __launch_bounds__(kThreads) void k1_prep_kernel(
     constexpr int AP = C + 4;              // padded LDS row of A / Ainv
     constexpr int NQ = kThreads / DK;      // row groups of the cumulative sum
     constexpr int RPQ = C / NQ;
+    typedef TIn tin8 __attribute__((ext_vector_type(8)));
 
     __shared__ __attribute__((aligned(16))) TIn sK[C][KP];
-    __shared__ __attribute__((aligned(16))) float sG[C][GP];  // G * log2(e)
+    __shared__ __attribute__((aligned(16))) float sG[C][GP];  // g, then G * log2(e)
     __shared__ __attribute__((aligned(16))) float sA[C][AP];  // A, then Ainv
     __shared__ float sB[C];
     __shared__ double sTot[NQ][DK];
@@ -280,27 +306,84 @@ __global__ __launch_bounds__(kThreads) void k1_prep_kernel(
 
     auto row_off = [&](int r) -> int64_t { return ((t0 + r) * H + h) * (int64_t)DK; };
 
-    // ---- stage K (zero rows past the chunk end), beta and the decay cumsum
-    for (int i = t; i < C * DK / VEC; i += kThreads) {
-        const int r = i / (DK / VEC);
-        const int c = (i % (DK / VEC)) * VEC;
-        typedef TIn vec_t __attribute__((ext_vector_type(VEC)));
-        vec_t val = {};
-        if (r < len) val = *reinterpret_cast<const vec_t*>(K + row_off(r) + c);
-        *reinterpret_cast<vec_t*>(&sK[r][c]) = val;
+    // ---- stage: K and g (zero past the chunk end), beta. Every load of the
+    // workgroup is issued before the first one is consumed.
+    typedef TIn vecK_t __attribute__((ext_vector_type(VEC)));
+    constexpr int KV = C * DK / VEC / kThreads;  // 16-byte K vectors per thread
+    constexpr int GV = C * DK / 4 / kThreads;    // 16-byte g vectors per thread
+    vecK_t kreg[KV];
+    f32x4 greg[GV];
+#pragma unroll
+    for (int u = 0; u < KV; ++u) {
+        const int i = t + u * kThreads;
+        const int r = i / (DK / VEC), c = (i % (DK / VEC)) * VEC;
+        kreg[u] = r < len ? *reinterpret_cast<const vecK_t*>(K + row_off(r) + c) : vecK_t{};
     }
-    if (t < C) sB[t] = t < len ? beta[(t0 + t) * H + h] : 0.f;
+#pragma unroll
+    for (int u = 0; u < GV; ++u) {
+        const int i = t + u * kThreads;
+        const int r = i / (DK / 4), c = (i % (DK / 4)) * 4;
+        greg[u] = r < len ? *reinterpret_cast<const f32x4*>(g + row_off(r) + c) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    const float breg = (t < C && t < len) ? beta[(t0 + t) * H + h] : 0.f;
+
+    // q values this wave needs later, prefetched now:
+    //   qa[gi][ks]: row 16*rb + m, channels 32ks + 8q .. +7 of the wave's row blocks
+    //   qd[i][0|1]: Qd handoff frag f = wave + 4i, channels 32ks + 4q .. +3 and + 16
+    typedef TIn tin8 __attribute__((ext_vector_type(8)));
+    typedef TIn tin4 __attribute__((ext_vector_type(4)));
+    const int plan[4][2][3] = {{{3, 0, 2}, {0, 0, 1}},   // {rb, sb_first, count}
+                               {{3, 2, 2}, {1, 0, 1}},
+                               {{2, 0, 2}, {-1, 0, 0}},
+                               {{2, 2, 1}, {1, 1, 1}}};
+    tin8 qa[2][NKS];
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi) {
+        const int rb = plan[wave][gi][0];
+        const int r = 16 * (rb < 0 ? 0 : rb) + m;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+            qa[gi][ks] = (rb >= 0 && r < len) ? *reinterpret_cast<const tin8*>(Q + row_off(r) + 32 * ks + 8 * q) : tin8{};
+    }
+    constexpr int QDF = 4 * NKS / 4;  // Qd frags per wave
+    tin4 qd[QDF][2];
+#pragma unroll
+    for (int i = 0; i < QDF; ++i) {
+        const int f = wave + 4 * i;
+        const int rt = f / NKS, ks = f % NKS;
+        const int r = 16 * rt + m;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+            qd[i][hh] = r < len ? *reinterpret_cast<const tin4*>(Q + row_off(r) + 32 * ks + 16 * hh + 4 * q) : tin4{};
+    }
+
+#pragma unroll
+    for (int u = 0; u < KV; ++u) {
+        const int i = t + u * kThreads;
+        const int r = i / (DK / VEC), c = (i % (DK / VEC)) * VEC;
+        *reinterpret_cast<vecK_t*>(&sK[r][c]) = kreg[u];
+    }
+#pragma unroll
+    for (int u = 0; u < GV; ++u) {
+        const int i = t + u * kThreads;
+        const int r = i / (DK / 4), c = (i % (DK / 4)) * 4;
+        *reinterpret_cast<f32x4*>(&sG[r][c]) = greg[u];
+    }
+    if (t < C) sB[t] = breg;
+    __syncthreads();
     {
+        // inclusive cumulative sum per channel in fp64 (rows past the end add 0)
         const int c = t % DK, grp = t / DK;
         double acc = 0.0;
-        for (int r = grp * RPQ; r < (grp + 1) * RPQ; ++r)
-            if (r < len) acc += (double)g[row_off(r) + c];
+#pragma unroll
+        for (int r = grp * RPQ; r < (grp + 1) * RPQ; ++r) acc += (double)sG[r][c];
         sTot[grp][c] = acc;
         __syncthreads();
         double run = 0.0;
         for (int p = 0; p < grp; ++p) run += sTot[p][c];
+#pragma unroll
         for (int r = grp * RPQ; r < (grp + 1) * RPQ; ++r) {
-            if (r < len) run += (double)g[row_off(r) + c];
+            run += (double)sG[r][c];
             sG[r][c] = (float)(run * 1.4426950408889634);
         }
     }
@@ -310,56 +393,62 @@ __global__ __launch_bounds__(kThreads) void k1_prep_kernel(
         if constexpr (BF16) return bf16_to_f32(sK[r][c]);
         else return sK[r][c];
     };
-    auto qval = [&](int r, int c) -> float {  // straight from global memory
-        if (r >= len) return 0.f;
-        if constexpr (BF16) return bf16_to_f32(Q[row_off(r) + c]);
-        else return Q[row_off(r) + c];
+    auto qf = [&](TIn v) -> float {
+        if constexpr (BF16) return bf16_to_f32(v);
+        else return v;
     };
 
-    // ---- phase A: A (strictly lower, into LDS) and P (handoff) per 16x16 block pair.
-    // Block pair (rb, sb), sb <= rb, uses reference row 16*rb: every factor
-    // e^(G_r - G_ref) (r >= ref) is <= 1 and e^(G_ref - G_s) is <= 1 for s < ref.
+    // ---- phase A: 16x16 block pairs (rb, sb), sb <= rb, reference row 16*rb:
+    // every factor e^(G_r - G_ref) (r >= ref) is <= 1 and e^(G_ref - G_s) is
+    // <= 1 for s < ref. Waves take the pairs grouped by rb so the row-block
+    // operands X = Kd', Z = Qd' are built once per rb.
     {
-        // pairs per wave, balanced: (rb, sb)
-        const int pairs[4][3][2] = {{{3, 0}, {3, 1}, {0, 0}},
-                                    {{3, 2}, {3, 3}, {1, 0}},
-                                    {{2, 0}, {2, 1}, {-1, -1}},
-                                    {{2, 2}, {1, 1}, {-1, -1}}};
-        for (int pi = 0; pi < 3; ++pi) {
-            const int rb = pairs[wave][pi][0], sb = pairs[wave][pi][1];
+#pragma unroll
+        for (int gi = 0; gi < 2; ++gi) {
+            const int rb = plan[wave][gi][0];
             if (rb < 0) break;
             const int ref = 16 * rb;
-            const int r = 16 * rb + m;  // row of the X / Z operands
-            const int s = 16 * sb + m;  // row of the Y operand
-            f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
+            const int r = 16 * rb + m;
+            Frag X[NKS], Z[NKS];
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
-                Frag X, Y, Z;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const int c = 32 * ks + 8 * q + e;
-                    const float gr = sG[r][c], gs = sG[s][c], gf = sG[ref][c];
-                    const float fr = exp2f(gr - gf);
-                    X[e] = (E)(kval(r, c) * fr);
-                    Z[e] = (E)(qval(r, c) * fr);
-                    Y[e] = (E)(kval(s, c) * exp2f(gf - gs));
+                    const float fr = fast_exp2(sG[r][c] - sG[ref][c]);
+                    X[ks][e] = (E)(kval(r, c) * fr);
+                    Z[ks][e] = (E)(qf(qa[gi][ks][e]) * fr);
                 }
-                accA = M::run(X, Y, accA);  // rows r, cols s
-                accP = M::run(Y, Z, accP);  // P^T: rows s, cols r
             }
-            // A[r'][s'] with r' = 16rb + 4q + i, s' = 16sb + m
+            for (int k2 = 0; k2 < plan[wave][gi][2]; ++k2) {
+                const int sb = plan[wave][gi][1] + k2;
+                const int s = 16 * sb + m;
+                f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int rr = 16 * rb + 4 * q + i, ss = 16 * sb + m;
-                sA[rr][ss] = ss < rr ? sB[rr] * accA[i] : 0.f;
-            }
-            // P^T[s'][r'] with s' = 16sb + 4q + i, r' = 16rb + m -> P A-frag
-            // [rt = rb][slab sb/2], slots 4*(sb%2) + i of lane (m + 16q).
-            E* pf = hb + HO::kP + ((size_t)(rb * 2 + sb / 2) * 64 + lane) * 8 + 4 * (sb % 2);
+                for (int ks = 0; ks < NKS; ++ks) {
+                    Frag Y;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int ss = 16 * sb + 4 * q + i, rr = 16 * rb + m;
-                pf[i] = (E)(ss <= rr ? accP[i] : 0.f);
+                    for (int e = 0; e < 8; ++e) {
+                        const int c = 32 * ks + 8 * q + e;
+                        Y[e] = (E)(kval(s, c) * fast_exp2(sG[ref][c] - sG[s][c]));
+                    }
+                    accA = M::run(X[ks], Y, accA);  // rows r, cols s
+                    accP = M::run(Y, Z[ks], accP);  // P^T: rows s, cols r
+                }
+                // A[r'][s'] with r' = 16rb + 4q + i, s' = 16sb + m
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int rr = 16 * rb + 4 * q + i, ss = 16 * sb + m;
+                    sA[rr][ss] = ss < rr ? sB[rr] * accA[i] : 0.f;
+                }
+                // P^T[s'][r'] with s' = 16sb + 4q + i, r' = 16rb + m -> P A-frag
+                // [rt = rb][slab sb/2], slots 4*(sb%2) + i of lane (m + 16q).
+                E* pf = hb + HO::kP + ((size_t)(rb * 2 + sb / 2) * 64 + lane) * 8 + 4 * (sb % 2);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int ss = 16 * sb + 4 * q + i, rr = 16 * rb + m;
+                    pf[i] = (E)(ss <= rr ? accP[i] : 0.f);
+                }
             }
         }
         // zero halves inside stored slabs: (rb, sb) = (0, 1) and (2, 3)
@@ -369,44 +458,23 @@ __global__ __launch_bounds__(kThreads) void k1_prep_kernel(
 #pragma unroll
             for (int i = 0; i < 4; ++i) pf[i] = (E)0.f;
         }
-    }
-    __syncthreads();
-
-    // ---- phase B: wave 0 inverts (I + A) by forward substitution, lane j =
-    // column j; the other waves write Qd, Kc^T and Gamma_last.
-    if (wave == 0) {
-        const int j = lane;
-        float x[C];
-#pragma unroll
-        for (int r = 0; r < C; ++r) {
-            float acc = (r == j) ? 1.f : 0.f;
-#pragma unroll
-            for (int s4 = 0; s4 < r / 4 * 4; s4 += 4) {
-                const f32x4 a4 = *reinterpret_cast<const f32x4*>(&sA[r][s4]);
-                acc -= a4[0] * x[s4] + a4[1] * x[s4 + 1] + a4[2] * x[s4 + 2] + a4[3] * x[s4 + 3];
-            }
-#pragma unroll
-            for (int s = r / 4 * 4; s < r; ++s) acc -= sA[r][s] * x[s];
-            x[r] = acc;
-        }
-        // all rows of A were consumed above: overwrite with Ainv (column j)
-#pragma unroll
-        for (int r = 0; r < C; ++r) sA[r][j] = x[r];
-    } else {
         // Qd A-frags: rows tokens (tile rt), K channels (slab ks, permuted)
-        for (int f = wave - 1; f < 4 * NKS; f += 3) {
+#pragma unroll
+        for (int i = 0; i < QDF; ++i) {
+            const int f = wave + 4 * i;
             const int rt = f / NKS, ks = f % NKS;
             const int r = 16 * rt + m;
+            // perm32(q, e): channels 32ks + 4q + e (e < 4) and 32ks + 16 + 4q + e - 4
             Frag out;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int c = 32 * ks + perm32(q, e);
-                out[e] = (E)(qval(r, c) * exp2f(sG[r][c]));
+                out[e] = (E)(qf(qd[i][e >> 2][e & 3]) * fast_exp2(sG[r][c]));
             }
             store_frag<Frag, E>(hb + HO::kQd, rt * NKS + ks, lane, out);
         }
         // Kc^T A-frags: rows channels (tile ct), K tokens (slab ts, permuted)
-        for (int f = wave - 1; f < NRT * 2; f += 3) {
+        for (int f = wave; f < NRT * 2; f += 4) {
             const int ct = f / 2, ts = f % 2;
             const int c = 16 * ct + m;
             const float gl = sG[C - 1][c];
@@ -414,45 +482,131 @@ __global__ __launch_bounds__(kThreads) void k1_prep_kernel(
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int r = 32 * ts + perm32(q, e);
-                out[e] = (E)(kval(r, c) * exp2f(gl - sG[r][c]));
+                out[e] = (E)(kval(r, c) * fast_exp2(gl - sG[r][c]));
             }
             store_frag<Frag, E>(hb + HO::kKc, ct * 2 + ts, lane, out);
         }
-        for (int c = t - 64; c < DK; c += kThreads - 64) glast[c] = exp2f(sG[C - 1][c]);
+        for (int c = t; c < DK; c += kThreads) glast[c] = fast_exp2(sG[C - 1][c]);
+    }
+    __syncthreads();
+
+    // ---- inverse: X = (I + A)^-1 in 16x16 blocks (all fp32).
+    // (1) wave b inverts the unit lower-triangular diagonal block I + A_bb by
+    //     forward substitution: lane (c = m, p = q) owns column c and sums the
+    //     terms s = 4u + p of each row; the four partial sums are combined with
+    //     two lane-pair exchanges (identical order in every lane). In place.
+    {
+        const int b = wave, c = m, p = q;
+        float xs[4] = {0.f, 0.f, 0.f, 0.f};  // xs[u] = x[4u + p][c]
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float acc = 0.f;
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if (4 * u < r) acc += sA[16 * b + r][16 * b + 4 * u + p] * xs[u];  // A_bb[r][s >= r] = 0
+            acc = pair_sum16(acc);
+            acc = pair_sum32(acc);
+            const float xr = (r == c ? 1.f : 0.f) - acc;
+            xs[r >> 2] = (p == (r & 3)) ? xr : xs[r >> 2];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) sA[16 * b + 4 * u + p][16 * b + c] = xs[u];
+    }
+    __syncthreads();
+    // (2) off-diagonal blocks, X_ij = -X_ii sum_{k=j}^{i-1} A_ik X_kj, by
+    //     distance i - j = 1, 2, 3 on v_mfma_f32_16x16x4_f32. K index of
+    //     instruction e in lane group g is 4g + e, so a result tile is the next
+    //     product's B operand as it stands. X_ij (i > j) is parked transposed
+    //     in the free upper block (j, i) until A is no longer needed.
+    {
+        auto mma_acc = [&](f32x4 acc, int i, int k, int j) -> f32x4 {  // acc += A_ik X_kj
+            const f32x4 av = *reinterpret_cast<const f32x4*>(&sA[16 * i + m][16 * k + 4 * q]);
+            f32x4 bv;
+            if (k == j) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) bv[e] = sA[16 * j + 4 * q + e][16 * j + m];
+            } else {
+                bv = *reinterpret_cast<const f32x4*>(&sA[16 * j + m][16 * k + 4 * q]);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[e], bv[e], acc, 0, 0, 0);
+            return acc;
+        };
+        auto finish = [&](const f32x4& T, int i, int j) {  // X_ij = -X_ii T, stored transposed
+            const f32x4 av = *reinterpret_cast<const f32x4*>(&sA[16 * i + m][16 * i + 4 * q]);
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[e], T[e], acc, 0, 0, 0);
+            *reinterpret_cast<f32x4*>(&sA[16 * j + m][16 * i + 4 * q]) = -acc;
+        };
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        if (wave < 3) {  // (1,0), (2,1), (3,2)
+            const int i = wave + 1, j = wave;
+            finish(mma_acc(z, i, j, j), i, j);
+        }
+        __syncthreads();
+        if (wave < 2) {  // (2,0), (3,1)
+            const int i = wave + 2, j = wave;
+            finish(mma_acc(mma_acc(z, i, j, j), i, j + 1, j), i, j);
+        }
+        __syncthreads();
+        if (wave == 0)  // (3,0)
+            finish(mma_acc(mma_acc(mma_acc(z, 3, 0, 0), 3, 1, 0), 3, 2, 0), 3, 0);
+        __syncthreads();
+        // move the parked blocks into the lower triangle and clear the upper one
+        const int blocks[6][2] = {{1, 0}, {2, 1}, {3, 2}, {2, 0}, {3, 1}, {3, 0}};
+        for (int idx = t; idx < 6 * 256; idx += kThreads) {
+            const int i = blocks[idx >> 8][0], j = blocks[idx >> 8][1];
+            const int r = (idx >> 4) & 15, c = idx & 15;
+            const float val = sA[16 * j + c][16 * i + r];
+            sA[16 * j + c][16 * i + r] = 0.f;
+            sA[16 * i + r][16 * j + c] = val;
+        }
     }
     __syncthreads();
 
     // ---- phase C: -W from W^T = (diag(beta) Kd)^T Ainv^T and the Ab handoff.
     // W^T tiles (channel tile ct, token tile rt); tiles 2ks and 2ks+1 of the
-    // same rt stack into the W A-frag of (rt, slab ks).
-    for (int f = wave; f < 4 * NKS; f += 4) {
-        const int ks = f % NKS, rt = f / NKS;
-        f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-        const int nts = rt >= 2 ? 2 : 1;  // Ainv[r][s] = 0 for s > r
-        for (int ts = 0; ts < nts; ++ts) {
-            Frag b;  // Ainv^T: column r = 16rt + m, K = s = 32ts + 8q + e
-            const int r = 16 * rt + m;
+    // same rt stack into the W A-frag of (rt, slab ks). Each wave keeps one ks.
+    {
+        const int ks = wave % NKS;
+        Frag aF[2][2];  // (beta Kd)^T: row c = 16(2ks+half) + m, K = s = 32ts + 8q + e
 #pragma unroll
-            for (int e = 0; e < 8; ++e) b[e] = (E)sA[r][32 * ts + 8 * q + e];
+        for (int half = 0; half < 2; ++half)
 #pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                Frag a;  // (beta Kd)^T: row c = 16(2ks+half) + m, K = s
+            for (int ts = 0; ts < 2; ++ts) {
                 const int c = 16 * (2 * ks + half) + m;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const int s = 32 * ts + 8 * q + e;
-                    a[e] = (E)(sB[s] * kval(s, c) * exp2f(sG[s][c]));
+                    aF[half][ts][e] = (E)(sB[s] * kval(s, c) * fast_exp2(sG[s][c]));
                 }
-                acc[half] = M::run(a, b, acc[half]);
             }
-        }
-        Frag out;
+        for (int f = wave; f < 4 * NKS; f += 4) {
+            const int rt = f / NKS;
+            f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+            const int nts = rt >= 2 ? 2 : 1;  // Ainv[r][s] = 0 for s > r
+            for (int ts = 0; ts < nts; ++ts) {
+                Frag b;  // Ainv^T: column r = 16rt + m, K = s = 32ts + 8q + e
+                const int r = 16 * rt + m;
+                const f32x4 b0 = *reinterpret_cast<const f32x4*>(&sA[r][32 * ts + 8 * q]);
+                const f32x4 b1 = *reinterpret_cast<const f32x4*>(&sA[r][32 * ts + 8 * q + 4]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            out[i] = (E)(-acc[0][i]);
-            out[4 + i] = (E)(-acc[1][i]);
+                for (int e = 0; e < 4; ++e) {
+                    b[e] = (E)b0[e];
+                    b[4 + e] = (E)b1[e];
+                }
+                acc[0] = M::run(aF[0][ts], b, acc[0]);
+                acc[1] = M::run(aF[1][ts], b, acc[1]);
+            }
+            Frag out;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                out[i] = (E)(-acc[0][i]);
+                out[4 + i] = (E)(-acc[1][i]);
+            }
+            store_frag<Frag, E>(hb + HO::kW, rt * NKS + ks, lane, out);
         }
-        store_frag<Frag, E>(hb + HO::kW, rt * NKS + ks, lane, out);
     }
     // Ab = Ainv diag(beta) A-frags: rows tokens (tile rt), K tokens (slab ts, permuted);
     // slabs (rt 0-1, ts 1) are identically zero and never read.
@@ -473,6 +627,22 @@ __global__ __launch_bounds__(kThreads) void k1_prep_kernel(
 }
 
 // ---------------------------------------------------------------- K2 -----
+// Per-wave operands of one chunk, loaded one chunk ahead of their use so the
+// scan never waits on memory: -W, Qd (row tile = wave), Ab, P (row tile =
+// wave, token slabs that can be non-zero), Kc^T (the wave's state row tiles),
+// Gamma_last for those rows, and this thread's share of the V tile.
+template <int DK, int NT, bool BF16>
+struct ChunkOps {
+    using Frag = typename Mma<BF16>::Frag;
+    using TIn = typename std::conditional<BF16, unsigned short, float>::type;
+    static constexpr int NKS = DK / 32;
+    static constexpr int TPW = DK / 64;
+    static constexpr int VPT = C * 16 * NT / kThreads;  // V elements per thread
+    Frag ab[2], wn[NKS], qd[NKS], p[2], kc[TPW][2];
+    f32x4 gl[TPW];
+    TIn v[VPT];
+};
+
 // One workgroup = one (sequence, head) and 16*NT value columns; wave w owns
 // U/O row tile w (tokens 16w..16w+15) and state row tiles w*TPW .. +TPW-1.
 template <int DK, int DV, int NT, bool BF16>
@@ -487,10 +657,12 @@ __global__ __launch_bounds__(kThreads) void k2_scan_kernel(
     using Frag = typename M::Frag;
     using TIn = typename std::conditional<BF16, unsigned short, float>::type;
     using HO = Handoff<DK, BF16>;
+    using Ops = ChunkOps<DK, NT, BF16>;
     constexpr int NKS = DK / 32;
     constexpr int TPW = DK / 64;            // state row tiles per wave
     constexpr int NVB = DV / (16 * NT);     // value-column blocks per (seq, head)
     constexpr int NV = 16 * NT;
+    constexpr int VPT = Ops::VPT;
 
     __shared__ __attribute__((aligned(32))) E sSh[NKS][NT][64][8];
     __shared__ __attribute__((aligned(32))) E sSl[BF16 ? NKS : 1][NT][64][8];
@@ -519,7 +691,42 @@ __global__ __launch_bounds__(kThreads) void k2_scan_kernel(
     const int wave = t >> 6;
     const int q = lane >> 4;
     const int m = lane & 15;
+    const int rt = wave;                  // U / O row tile
+    const int nts = rt >= 2 ? 2 : 1;      // token slabs of P / Ab that can be non-zero
     const TIn* V = static_cast<const TIn*>(vin);
+
+    // Issue every load of chunk n (always in bounds: callers clamp n).
+    auto load_ops = [&](Ops& op, int n) {
+        const E* hb = reinterpret_cast<const E*>(handoff + ((size_t)h * max_chunks + cbase + n) * HO::kBytes);
+        const float* glast = reinterpret_cast<const float*>(reinterpret_cast<const unsigned char*>(hb) + HO::kGlastBytes);
+#pragma unroll
+        for (int ts = 0; ts < 2; ++ts) {
+            if (ts < nts) {
+                op.ab[ts] = load_frag<Frag, E>(hb + HO::kAb, rt * 2 + ts, lane);
+                op.p[ts] = load_frag<Frag, E>(hb + HO::kP, rt * 2 + ts, lane);
+            }
+        }
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            op.wn[ks] = load_frag<Frag, E>(hb + HO::kW, rt * NKS + ks, lane);
+            op.qd[ks] = load_frag<Frag, E>(hb + HO::kQd, rt * NKS + ks, lane);
+        }
+#pragma unroll
+        for (int i = 0; i < TPW; ++i) {
+            const int srt = wave * TPW + i;
+            op.kc[i][0] = load_frag<Frag, E>(hb + HO::kKc, srt * 2 + 0, lane);
+            op.kc[i][1] = load_frag<Frag, E>(hb + HO::kKc, srt * 2 + 1, lane);
+            op.gl[i] = *reinterpret_cast<const f32x4*>(glast + 16 * srt + 4 * q);
+        }
+        const int64_t tok0 = tstart + (int64_t)n * C;
+        const int64_t left = L - (int64_t)n * C;
+#pragma unroll
+        for (int e = 0; e < VPT; ++e) {
+            const int idx = t + e * kThreads;
+            const int s = idx / NV, col = idx % NV;
+            op.v[e] = s < left ? V[((tok0 + s) * H + h) * (int64_t)DV + j0 + col] : (TIn)0;
+        }
+    };
 
     // state rows owned: channel 16*rt + 4q + i, column j0 + 16ct + m
     f32x4 S[TPW][NT];
@@ -534,70 +741,67 @@ __global__ __launch_bounds__(kThreads) void k2_scan_kernel(
                 S[i][ct][ii] = s0 ? s0[sbase + (size_t)row * DV + j0 + 16 * ct + m] : 0.f;
             }
 
+    Ops cur, nxt;
+    if (nch > 0) load_ops(cur, 0);
     for (int n = 0; n < nch; ++n) {
-        const E* hb = reinterpret_cast<const E*>(handoff + ((size_t)h * max_chunks + cbase + n) * HO::kBytes);
-        const float* glast = reinterpret_cast<const float*>(reinterpret_cast<const unsigned char*>(hb) + HO::kGlastBytes);
+        load_ops(nxt, n + 1 < nch ? n + 1 : n);  // prefetch (the last one is a harmless repeat)
         const int64_t tok0 = tstart + (int64_t)n * C;
         const int len = (int)((L - (int64_t)n * C) < C ? (L - (int64_t)n * C) : C);
 
-        // (a) publish S as B-frags (slab = row tile / 2, half = row tile % 2) and stage V
+        // (a) publish S as B-frags (slab = row tile / 2, half = row tile % 2) and the V tile
 #pragma unroll
         for (int i = 0; i < TPW; ++i) {
-            const int rt = wave * TPW + i;
+            const int srt = wave * TPW + i;
 #pragma unroll
             for (int ct = 0; ct < NT; ++ct) {
-                E* ph = &sSh[rt / 2][ct][lane][4 * (rt % 2)];
 #pragma unroll
                 for (int ii = 0; ii < 4; ++ii) {
                     const E hi = (E)S[i][ct][ii];
-                    ph[ii] = hi;
-                    if constexpr (BF16) sSl[rt / 2][ct][lane][4 * (rt % 2) + ii] = (E)(S[i][ct][ii] - (float)hi);
+                    sSh[srt / 2][ct][lane][4 * (srt % 2) + ii] = hi;
+                    if constexpr (BF16) sSl[srt / 2][ct][lane][4 * (srt % 2) + ii] = (E)(S[i][ct][ii] - (float)hi);
                 }
             }
         }
-        for (int idx = t; idx < C * NV; idx += kThreads) {
+#pragma unroll
+        for (int e = 0; e < VPT; ++e) {
+            const int idx = t + e * kThreads;
             const int s = idx / NV, col = idx % NV;
-            float val = 0.f;
-            if (s < len) {
-                const int64_t off = ((tok0 + s) * H + h) * (int64_t)DV + j0 + col;
-                if constexpr (BF16) val = bf16_to_f32(V[off]);
-                else val = V[off];
-            }
             const int ts = s >> 5, w32 = s & 31;
             const int qq = (w32 & 15) >> 2;
-            const int e = (w32 & 3) + ((w32 >> 4) << 2);
-            sV[ts][col >> 4][(col & 15) + 16 * qq][e] = (E)val;
+            const int ee = (w32 & 3) + ((w32 >> 4) << 2);
+            float val;
+            if constexpr (BF16) val = bf16_to_f32(cur.v[e]);
+            else val = cur.v[e];
+            sV[ts][col >> 4][(col & 15) + 16 * qq][ee] = (E)val;
         }
         __syncthreads();
 
         // (c) U = Ab V - W S ; O = Qd S  (row tile = wave)
-        const int rt = wave;
-        const int nts = rt >= 2 ? 2 : 1;
         f32x4 U[NT], O[NT];
 #pragma unroll
         for (int ct = 0; ct < NT; ++ct) {
             U[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
             O[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
-        for (int ts = 0; ts < nts; ++ts) {
-            const Frag a = load_frag<Frag, E>(hb + HO::kAb, rt * 2 + ts, lane);
 #pragma unroll
-            for (int ct = 0; ct < NT; ++ct)
-                U[ct] = M::run(a, *reinterpret_cast<const Frag*>(&sV[ts][ct][lane][0]), U[ct]);
+        for (int ts = 0; ts < 2; ++ts) {
+            if (ts < nts) {
+#pragma unroll
+                for (int ct = 0; ct < NT; ++ct)
+                    U[ct] = M::run(cur.ab[ts], *reinterpret_cast<const Frag*>(&sV[ts][ct][lane][0]), U[ct]);
+            }
         }
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
-            const Frag aw = load_frag<Frag, E>(hb + HO::kW, rt * NKS + ks, lane);
-            const Frag aq = load_frag<Frag, E>(hb + HO::kQd, rt * NKS + ks, lane);
 #pragma unroll
             for (int ct = 0; ct < NT; ++ct) {
                 const Frag sh = *reinterpret_cast<const Frag*>(&sSh[ks][ct][lane][0]);
-                U[ct] = M::run(aw, sh, U[ct]);
-                O[ct] = M::run(aq, sh, O[ct]);
+                U[ct] = M::run(cur.wn[ks], sh, U[ct]);
+                O[ct] = M::run(cur.qd[ks], sh, O[ct]);
                 if constexpr (BF16) {
                     const Frag sl = *reinterpret_cast<const Frag*>(&sSl[ks][ct][lane][0]);
-                    U[ct] = M::run(aw, sl, U[ct]);
-                    O[ct] = M::run(aq, sl, O[ct]);
+                    U[ct] = M::run(cur.wn[ks], sl, U[ct]);
+                    O[ct] = M::run(cur.qd[ks], sl, O[ct]);
                 }
             }
         }
@@ -609,11 +813,13 @@ __global__ __launch_bounds__(kThreads) void k2_scan_kernel(
         __syncthreads();
 
         // (f) O += P U and store the valid rows
-        for (int ts = 0; ts < nts; ++ts) {
-            const Frag a = load_frag<Frag, E>(hb + HO::kP, rt * 2 + ts, lane);
 #pragma unroll
-            for (int ct = 0; ct < NT; ++ct)
-                O[ct] = M::run(a, *reinterpret_cast<const Frag*>(&sU[ts][ct][lane][0]), O[ct]);
+        for (int ts = 0; ts < 2; ++ts) {
+            if (ts < nts) {
+#pragma unroll
+                for (int ct = 0; ct < NT; ++ct)
+                    O[ct] = M::run(cur.p[ts], *reinterpret_cast<const Frag*>(&sU[ts][ct][lane][0]), O[ct]);
+            }
         }
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
@@ -628,23 +834,19 @@ __global__ __launch_bounds__(kThreads) void k2_scan_kernel(
         // (g) S <- diag(Gamma_last) S + Kc^T U
 #pragma unroll
         for (int i = 0; i < TPW; ++i) {
-            const int srt = wave * TPW + i;
-            const f32x4 gl = *reinterpret_cast<const f32x4*>(glast + 16 * srt + 4 * q);
-            const Frag a0 = load_frag<Frag, E>(hb + HO::kKc, srt * 2 + 0, lane);
-            const Frag a1 = load_frag<Frag, E>(hb + HO::kKc, srt * 2 + 1, lane);
 #pragma unroll
             for (int ct = 0; ct < NT; ++ct) {
-                f32x4 acc = S[i][ct] * gl;
-                acc = M::run(a0, *reinterpret_cast<const Frag*>(&sU[0][ct][lane][0]), acc);
-                acc = M::run(a1, *reinterpret_cast<const Frag*>(&sU[1][ct][lane][0]), acc);
+                f32x4 acc = S[i][ct] * cur.gl[i];
+                acc = M::run(cur.kc[i][0], *reinterpret_cast<const Frag*>(&sU[0][ct][lane][0]), acc);
+                acc = M::run(cur.kc[i][1], *reinterpret_cast<const Frag*>(&sU[1][ct][lane][0]), acc);
                 S[i][ct] = acc;
             }
         }
 
         // (h) checkpoint after every `interval` tokens of the sequence
-        const int64_t done = (int64_t)(n + 1) * C;
         // (without cu_seqlens the only sequence has checkpoint base 0; rows the
         // caller's buffer does not have are skipped)
+        const int64_t done = (int64_t)(n + 1) * C;
         const int64_t cidx = interval > 0 ? (int64_t)(ckpt_base ? ckpt_base[seq] : 0) + done / interval - 1 : -1;
         if (interval > 0 && done <= L && done % interval == 0 && cidx < ckpt_rows) {
             float* cp = ckpt + (cidx * H + h) * (size_t)DK * DV;
@@ -658,6 +860,7 @@ __global__ __launch_bounds__(kThreads) void k2_scan_kernel(
                         cp[(size_t)row * DV + j0 + 16 * ct + m] = S[i][ct][ii];
                     }
         }
+        cur = nxt;
     }
 
     if (sfinal) {
@@ -697,10 +900,11 @@ template <int DK, int DV, bool BF16>
 hipError_t launch_typed(const PrefillArgs& a, hipStream_t stream) {
     const Plan p = make_plan(a);
     const bool varlen = a.cu_seqlens != nullptr;
-    if (varlen)
+    const bool prepare = (a.phases & 1u) != 0, scan = (a.phases & 2u) != 0;
+    if (prepare && varlen)
         hipLaunchKernelGGL(prep_kernel, dim3(1), dim3(kThreads), 0, stream, a.cu_seqlens, a.num_seqs,
                            a.total_tokens, a.ckpt_interval, p.chunk_start, p.ckpt_base, p.order);
-    if (p.max_chunks > 0 && a.total_tokens > 0)
+    if (prepare && p.max_chunks > 0 && a.total_tokens > 0)
         hipLaunchKernelGGL((k1_prep_kernel<DK, BF16>), dim3((unsigned)p.max_chunks, (unsigned)a.H),
                            dim3(kThreads), 0, stream, a.q, a.k, a.g, a.beta, a.cu_seqlens,
                            varlen ? p.chunk_start : nullptr, a.num_seqs, a.total_tokens, a.H,
@@ -710,7 +914,8 @@ hipError_t launch_typed(const PrefillArgs& a, hipStream_t stream) {
     const int npairs = a.num_seqs * a.H;
     const int64_t groups = (npairs + 7) / 8;
     const unsigned grid = (unsigned)(groups * 8 * NVB);
-    hipLaunchKernelGGL((k2_scan_kernel<DK, DV, NT, BF16>), dim3(grid), dim3(kThreads), 0, stream,
+    if (scan)
+        hipLaunchKernelGGL((k2_scan_kernel<DK, DV, NT, BF16>), dim3(grid), dim3(kThreads), 0, stream,
                        a.v, a.cu_seqlens, varlen ? p.order : nullptr,
                        varlen ? p.chunk_start : nullptr, varlen ? p.ckpt_base : nullptr, npairs,
                        a.total_tokens, a.H, p.max_chunks, p.handoff, a.initial_state, a.final_state,

@@ -85,6 +85,13 @@ def test_prefill_validation(kw, status):
     assert prefill(**kw) == status
 
 
+@pytest.mark.parametrize("phases,status", [(0, INV), (4, INV), (7, INV)])
+def test_prefill_phases_validation(phases, status):
+    st = B.prefill_phases_raw(A, A, A, B.KDA_BF16, A, A, None, 1, 256, 2, 128, 128, 64, None, A,
+                              0, None, 0, A, A, 10 ** 12, phases, None)
+    assert st == status
+
+
 def test_prefill_workspace_exact_boundary():
     need = ws_size(256, 1, 2, 128, 128)
     assert prefill(wsb=need - 1) == WS
