@@ -140,9 +140,10 @@ def bench_decode(steps, warmup):
                 bytes=byts, flops=Bsz * H * acc.decode_flops_per_head_token(D, D))
 
 
-def cpu_baseline(x, target_s=15.0):
-    """fp64 oracle on all 8192 tokens of a few heads (all value columns),
-    extrapolated to the whole workload's tokens/s."""
+def cpu_baseline(x, target_s=10.0):
+    """fp64 oracle (all value columns of a growing set of heads, all tokens),
+    timed until about target_s seconds of CPU work; reports the median
+    per-head time scaled to the whole workload."""
     import numpy as np
     from oracle import recurrence
 
@@ -157,13 +158,18 @@ def cpu_baseline(x, target_s=15.0):
 
     t1 = run([0])
     n = int(max(1, min(x.H, round(target_s / max(t1, 1e-3)))))
-    tn = run(list(range(n)))
-    per_head = tn / n
-    full = per_head * x.H
+    per_head, spent, reps = [], 0.0, 0
+    while spent < target_s and reps < 100:
+        tn = run(list(range(n)))
+        per_head.append(tn / n)
+        spent += tn
+        reps += 1
+    full = float(np.median(per_head)) * x.H
     return dict(value=x.total_tokens / full / 1e6, unit="Mtok/s", cores=cores, kind="oracle",
                 sample=f"all {x.total_tokens} tokens x {n} of {x.H} heads x all {x.Dv} value "
-                       f"columns, fp64 token recurrence, {tn:.1f} s; scaled to {x.H} heads",
-                seconds=tn)
+                       f"columns, fp64 token recurrence, repeated {reps}x ({spent:.1f} s); "
+                       f"median scaled to {x.H} heads",
+                seconds=spent)
 
 
 def roofline(bytes_, ms, traffic=None):
@@ -180,6 +186,9 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=64)
     ap.add_argument("--only", choices=["all", "prefill", "decode"], default="all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="first run one device-to-device copy of this many MiB (a known-size "
+                         "reference dispatch for hardware traffic counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -196,6 +205,14 @@ def main():
         sys.exit(1)
     import linear_attention_05_amd as K
     K.load_library()
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib * (1 << 20) // 4
+        src = torch.ones(n, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     out = {}
     if args.only in ("all", "prefill"):

@@ -143,8 +143,13 @@ __device__ __forceinline__ void store_frag(E* base, int frag, int lane, const Fr
 }
 
 // Workspace: [chunk_start: S+1][ckpt_base: S+1][order: S] int32, padded to
-// 256 bytes, then the handoff blocks [H][max_chunks].
-size_t table_bytes(int num_seqs) { return ((size_t)(3 * num_seqs + 2) * 4 + 255) / 256 * 256; }
+// 256 bytes, a sink for stores the scan issues without a branch but does not
+// need (512 KiB: 64 workgroup slots x 256 threads x 8 floats), then the handoff
+// blocks [H][max_chunks].
+constexpr int kSinkSlots = 64;     // workgroup slots (power of two)
+constexpr int kSinkFloats = 8;     // floats per thread and slot
+constexpr size_t kSinkBytes = (size_t)kSinkSlots * kThreads * kSinkFloats * sizeof(float);
+size_t table_bytes(int num_seqs) { return ((size_t)(3 * num_seqs + 2) * 4 + 255) / 256 * 256 + kSinkBytes; }
 
 // Token range [start, start + len) of sequence s, clamped to [0, N) so that a
 // malformed cu_seqlens can never send an access out of bounds.
@@ -458,6 +463,12 @@ __global__ __launch_bounds__(kThreads) void k1_prep_kernel(
 #pragma unroll
             for (int i = 0; i < 4; ++i) pf[i] = (E)0.f;
         }
+        // whole zero slabs (row tiles 0-1, token slab 1) of P and Ab
+        if (wave < 2) {
+            const Frag zf = {};
+            store_frag<Frag, E>(hb + HO::kP, wave * 2 + 1, lane, zf);
+            store_frag<Frag, E>(hb + HO::kAb, wave * 2 + 1, lane, zf);
+        }
         // Qd A-frags: rows tokens (tile rt), K channels (slab ks, permuted)
 #pragma unroll
         for (int i = 0; i < QDF; ++i) {
@@ -609,7 +620,7 @@ __global__ __launch_bounds__(kThreads) void k1_prep_kernel(
         }
     }
     // Ab = Ainv diag(beta) A-frags: rows tokens (tile rt), K tokens (slab ts, permuted);
-    // slabs (rt 0-1, ts 1) are identically zero and never read.
+    // slabs (rt 0-1, ts 1) are identically zero (written in phase A).
     {
         const int frags[6][2] = {{0, 0}, {1, 0}, {2, 0}, {2, 1}, {3, 0}, {3, 1}};
         for (int f = wave; f < 6; f += 4) {
@@ -627,47 +638,52 @@ __global__ __launch_bounds__(kThreads) void k1_prep_kernel(
 }
 
 // ---------------------------------------------------------------- K2 -----
-// Per-wave operands of one chunk, loaded one chunk ahead of their use so the
-// scan never waits on memory: -W, Qd (row tile = wave), Ab, P (row tile =
-// wave, token slabs that can be non-zero), Kc^T (the wave's state row tiles),
-// Gamma_last for those rows, and this thread's share of the V tile.
+// Per-wave operands of one chunk: -W, Qd (row tile = wave), Ab, P (row tile =
+// wave; both token slabs, the second is zero for row tiles 0-1), Kc^T (the
+// wave's state row tiles), Gamma_last for those rows, and this thread's share
+// of the V tile.
 template <int DK, int NT, bool BF16>
 struct ChunkOps {
     using Frag = typename Mma<BF16>::Frag;
     using TIn = typename std::conditional<BF16, unsigned short, float>::type;
+    typedef TIn tin4 __attribute__((ext_vector_type(4)));
     static constexpr int NKS = DK / 32;
     static constexpr int TPW = DK / 64;
-    static constexpr int VPT = C * 16 * NT / kThreads;  // V elements per thread
     Frag ab[2], wn[NKS], qd[NKS], p[2], kc[TPW][2];
     f32x4 gl[TPW];
-    TIn v[VPT];
+    tin4 v[NT];
 };
 
 // One workgroup = one (sequence, head) and 16*NT value columns; wave w owns
 // U/O row tile w (tokens 16w..16w+15) and state row tiles w*TPW .. +TPW-1.
+// The operands of chunk n + 2 are requested while chunk n computes, in three
+// rotating register buffers. The chunk loop has no branches (loads are
+// unconditional, a token past the end of a sequence stores to a sink), so the
+// compiler's memory-wait analysis stays exact and the prefetches stay in
+// flight; outputs leave as one 16-byte store per lane and 16-column tile.
 template <int DK, int DV, int NT, bool BF16>
 __global__ __launch_bounds__(kThreads) void k2_scan_kernel(
     const void* __restrict__ vin, const int32_t* __restrict__ cu, const int32_t* __restrict__ order,
     const int32_t* __restrict__ chunk_start, const int32_t* __restrict__ ckpt_base, int npairs,
     int64_t N, int H, int64_t max_chunks, const unsigned char* __restrict__ handoff,
     const float* __restrict__ s0, float* __restrict__ sfinal, int64_t interval,
-    float* __restrict__ ckpt, int64_t ckpt_rows, float* __restrict__ o) {
+    float* __restrict__ ckpt, int64_t ckpt_rows, float* __restrict__ o, float* __restrict__ sink) {
     using M = Mma<BF16>;
     using E = typename M::E;
     using Frag = typename M::Frag;
     using TIn = typename std::conditional<BF16, unsigned short, float>::type;
     using HO = Handoff<DK, BF16>;
     using Ops = ChunkOps<DK, NT, BF16>;
+    using tin4 = typename Ops::tin4;
+    typedef E e4 __attribute__((ext_vector_type(4)));
     constexpr int NKS = DK / 32;
     constexpr int TPW = DK / 64;            // state row tiles per wave
     constexpr int NVB = DV / (16 * NT);     // value-column blocks per (seq, head)
     constexpr int NV = 16 * NT;
-    constexpr int VPT = Ops::VPT;
 
-    __shared__ __attribute__((aligned(32))) E sSh[NKS][NT][64][8];
-    __shared__ __attribute__((aligned(32))) E sSl[BF16 ? NKS : 1][NT][64][8];
-    __shared__ __attribute__((aligned(32))) E sV[2][NT][64][8];
-    __shared__ __attribute__((aligned(32))) E sU[2][NT][64][8];
+    __shared__ __attribute__((aligned(32))) E sS[NKS][NT][64][8];  // S(n) as B-frags
+    __shared__ __attribute__((aligned(32))) E sV[2][NT][64][8];    // V(n) as B-frags
+    __shared__ __attribute__((aligned(32))) E sU[2][NT][64][8];    // U(n) as B-frags
 
     // XCD-aware mapping: the NVB column blocks of one (seq, head) share an
     // XCD (workgroups are dealt to the 8 XCDs round-robin), so their common
@@ -685,6 +701,7 @@ __global__ __launch_bounds__(kThreads) void k2_scan_kernel(
     int nch = (int)((L + C - 1) / C);
     if (cbase + (int64_t)nch > max_chunks) nch = cbase < max_chunks ? (int)(max_chunks - cbase) : 0;
     const int j0 = vb * NV;
+    const int64_t cpbase = ckpt_base ? ckpt_base[seq] : 0;  // one sequence: base 0
 
     const int t = threadIdx.x;
     const int lane = t & 63;
@@ -692,19 +709,21 @@ __global__ __launch_bounds__(kThreads) void k2_scan_kernel(
     const int q = lane >> 4;
     const int m = lane & 15;
     const int rt = wave;                  // U / O row tile
-    const int nts = rt >= 2 ? 2 : 1;      // token slabs of P / Ab that can be non-zero
     const TIn* V = static_cast<const TIn*>(vin);
+    // V tile: thread t stages token vs = t / 4, columns 16ct + 4*(t % 4) .. +3
+    const int vs = t >> 2, vc = 4 * (t & 3);
+    // this lane's private sink slot (stores that must not land anywhere)
+    float* my_sink = sink + ((size_t)(id & (kSinkSlots - 1)) * kThreads + t) * kSinkFloats;
+    const unsigned char* hbase = handoff + ((size_t)h * max_chunks + cbase) * HO::kBytes;
 
-    // Issue every load of chunk n (always in bounds: callers clamp n).
+    // Issue every load of chunk n (0 <= n < nch: in bounds).
     auto load_ops = [&](Ops& op, int n) {
-        const E* hb = reinterpret_cast<const E*>(handoff + ((size_t)h * max_chunks + cbase + n) * HO::kBytes);
+        const E* hb = reinterpret_cast<const E*>(hbase + (size_t)n * HO::kBytes);
         const float* glast = reinterpret_cast<const float*>(reinterpret_cast<const unsigned char*>(hb) + HO::kGlastBytes);
 #pragma unroll
         for (int ts = 0; ts < 2; ++ts) {
-            if (ts < nts) {
-                op.ab[ts] = load_frag<Frag, E>(hb + HO::kAb, rt * 2 + ts, lane);
-                op.p[ts] = load_frag<Frag, E>(hb + HO::kP, rt * 2 + ts, lane);
-            }
+            op.ab[ts] = load_frag<Frag, E>(hb + HO::kAb, rt * 2 + ts, lane);
+            op.p[ts] = load_frag<Frag, E>(hb + HO::kP, rt * 2 + ts, lane);
         }
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
@@ -718,35 +737,47 @@ __global__ __launch_bounds__(kThreads) void k2_scan_kernel(
             op.kc[i][1] = load_frag<Frag, E>(hb + HO::kKc, srt * 2 + 1, lane);
             op.gl[i] = *reinterpret_cast<const f32x4*>(glast + 16 * srt + 4 * q);
         }
-        const int64_t tok0 = tstart + (int64_t)n * C;
+        // token rows past the end read the last valid row (zeroed when staged)
         const int64_t left = L - (int64_t)n * C;
-#pragma unroll
-        for (int e = 0; e < VPT; ++e) {
-            const int idx = t + e * kThreads;
-            const int s = idx / NV, col = idx % NV;
-            op.v[e] = s < left ? V[((tok0 + s) * H + h) * (int64_t)DV + j0 + col] : (TIn)0;
-        }
-    };
-
-    // state rows owned: channel 16*rt + 4q + i, column j0 + 16ct + m
-    f32x4 S[TPW][NT];
-    const size_t sbase = ((size_t)seq * H + h) * DK * DV;
-#pragma unroll
-    for (int i = 0; i < TPW; ++i)
+        const int64_t tok = tstart + (int64_t)n * C + (vs < left ? vs : left - 1);
 #pragma unroll
         for (int ct = 0; ct < NT; ++ct)
-#pragma unroll
-            for (int ii = 0; ii < 4; ++ii) {
-                const int row = 16 * (wave * TPW + i) + 4 * q + ii;
-                S[i][ct][ii] = s0 ? s0[sbase + (size_t)row * DV + j0 + 16 * ct + m] : 0.f;
-            }
+            op.v[ct] = *reinterpret_cast<const tin4*>(V + (tok * H + h) * (int64_t)DV + j0 + 16 * ct + vc);
+    };
 
-    Ops cur, nxt;
-    if (nch > 0) load_ops(cur, 0);
-    for (int n = 0; n < nch; ++n) {
-        load_ops(nxt, n + 1 < nch ? n + 1 : n);  // prefetch (the last one is a harmless repeat)
+    // state rows owned: channel 16*srt + 4q + i, column j0 + 16ct + m
+    f32x4 S[TPW][NT];
+    const size_t sbase = ((size_t)seq * H + h) * DK * DV;
+    if (s0) {
+#pragma unroll
+        for (int i = 0; i < TPW; ++i)
+#pragma unroll
+            for (int ct = 0; ct < NT; ++ct)
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii)
+                    S[i][ct][ii] = s0[sbase + (size_t)(16 * (wave * TPW + i) + 4 * q + ii) * DV + j0 + 16 * ct + m];
+    } else {
+#pragma unroll
+        for (int i = 0; i < TPW; ++i)
+#pragma unroll
+            for (int ct = 0; ct < NT; ++ct) S[i][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    auto store_state = [&](float* dst) {
+#pragma unroll
+        for (int i = 0; i < TPW; ++i)
+#pragma unroll
+            for (int ct = 0; ct < NT; ++ct)
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii)
+                    dst[(size_t)(16 * (wave * TPW + i) + 4 * q + ii) * DV + j0 + 16 * ct + m] = S[i][ct][ii];
+    };
+
+    // One chunk step with operands `cur` (chunk n).
+    auto step = [&](const Ops& cur, int n) {
         const int64_t tok0 = tstart + (int64_t)n * C;
-        const int len = (int)((L - (int64_t)n * C) < C ? (L - (int64_t)n * C) : C);
+        const int64_t left = L - (int64_t)n * C;
+        const int len = left < C ? (int)left : C;
 
         // (a) publish S as B-frags (slab = row tile / 2, half = row tile % 2) and the V tile
 #pragma unroll
@@ -754,126 +785,116 @@ __global__ __launch_bounds__(kThreads) void k2_scan_kernel(
             const int srt = wave * TPW + i;
 #pragma unroll
             for (int ct = 0; ct < NT; ++ct) {
+                e4 v4;
 #pragma unroll
-                for (int ii = 0; ii < 4; ++ii) {
-                    const E hi = (E)S[i][ct][ii];
-                    sSh[srt / 2][ct][lane][4 * (srt % 2) + ii] = hi;
-                    if constexpr (BF16) sSl[srt / 2][ct][lane][4 * (srt % 2) + ii] = (E)(S[i][ct][ii] - (float)hi);
-                }
+                for (int ii = 0; ii < 4; ++ii) v4[ii] = (E)S[i][ct][ii];
+                *reinterpret_cast<e4*>(&sS[srt / 2][ct][lane][4 * (srt % 2)]) = v4;
             }
         }
-#pragma unroll
-        for (int e = 0; e < VPT; ++e) {
-            const int idx = t + e * kThreads;
-            const int s = idx / NV, col = idx % NV;
-            const int ts = s >> 5, w32 = s & 31;
+        {
+            // token vs -> slab vs/32, B-frag lane (col & 15) + 16 * qq, slot ee (inverse of perm32)
+            const int ts = vs >> 5, w32 = vs & 31;
             const int qq = (w32 & 15) >> 2;
             const int ee = (w32 & 3) + ((w32 >> 4) << 2);
-            float val;
-            if constexpr (BF16) val = bf16_to_f32(cur.v[e]);
-            else val = cur.v[e];
-            sV[ts][col >> 4][(col & 15) + 16 * qq][ee] = (E)val;
-        }
-        __syncthreads();
-
-        // (c) U = Ab V - W S ; O = Qd S  (row tile = wave)
-        f32x4 U[NT], O[NT];
-#pragma unroll
-        for (int ct = 0; ct < NT; ++ct) {
-            U[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-            O[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-#pragma unroll
-        for (int ts = 0; ts < 2; ++ts) {
-            if (ts < nts) {
-#pragma unroll
-                for (int ct = 0; ct < NT; ++ct)
-                    U[ct] = M::run(cur.ab[ts], *reinterpret_cast<const Frag*>(&sV[ts][ct][lane][0]), U[ct]);
-            }
-        }
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-#pragma unroll
-            for (int ct = 0; ct < NT; ++ct) {
-                const Frag sh = *reinterpret_cast<const Frag*>(&sSh[ks][ct][lane][0]);
-                U[ct] = M::run(cur.wn[ks], sh, U[ct]);
-                O[ct] = M::run(cur.qd[ks], sh, O[ct]);
-                if constexpr (BF16) {
-                    const Frag sl = *reinterpret_cast<const Frag*>(&sSl[ks][ct][lane][0]);
-                    U[ct] = M::run(cur.wn[ks], sl, U[ct]);
-                    O[ct] = M::run(cur.qd[ks], sl, O[ct]);
-                }
-            }
-        }
-        // (d) publish U as B-frags (K = tokens): slab rt/2, half rt%2
-#pragma unroll
-        for (int ct = 0; ct < NT; ++ct)
-#pragma unroll
-            for (int ii = 0; ii < 4; ++ii) sU[rt / 2][ct][lane][4 * (rt % 2) + ii] = (E)U[ct][ii];
-        __syncthreads();
-
-        // (f) O += P U and store the valid rows
-#pragma unroll
-        for (int ts = 0; ts < 2; ++ts) {
-            if (ts < nts) {
-#pragma unroll
-                for (int ct = 0; ct < NT; ++ct)
-                    O[ct] = M::run(cur.p[ts], *reinterpret_cast<const Frag*>(&sU[ts][ct][lane][0]), O[ct]);
-            }
-        }
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-            const int tok = 16 * rt + 4 * q + ii;
-            if (tok < len) {
-                float* op = o + ((tok0 + tok) * H + h) * (int64_t)DV + j0 + m;
-#pragma unroll
-                for (int ct = 0; ct < NT; ++ct) op[16 * ct] = O[ct][ii];
-            }
-        }
-
-        // (g) S <- diag(Gamma_last) S + Kc^T U
-#pragma unroll
-        for (int i = 0; i < TPW; ++i) {
-#pragma unroll
-            for (int ct = 0; ct < NT; ++ct) {
-                f32x4 acc = S[i][ct] * cur.gl[i];
-                acc = M::run(cur.kc[i][0], *reinterpret_cast<const Frag*>(&sU[0][ct][lane][0]), acc);
-                acc = M::run(cur.kc[i][1], *reinterpret_cast<const Frag*>(&sU[1][ct][lane][0]), acc);
-                S[i][ct] = acc;
-            }
-        }
-
-        // (h) checkpoint after every `interval` tokens of the sequence
-        // (without cu_seqlens the only sequence has checkpoint base 0; rows the
-        // caller's buffer does not have are skipped)
-        const int64_t done = (int64_t)(n + 1) * C;
-        const int64_t cidx = interval > 0 ? (int64_t)(ckpt_base ? ckpt_base[seq] : 0) + done / interval - 1 : -1;
-        if (interval > 0 && done <= L && done % interval == 0 && cidx < ckpt_rows) {
-            float* cp = ckpt + (cidx * H + h) * (size_t)DK * DV;
-#pragma unroll
-            for (int i = 0; i < TPW; ++i)
-#pragma unroll
-                for (int ct = 0; ct < NT; ++ct)
-#pragma unroll
-                    for (int ii = 0; ii < 4; ++ii) {
-                        const int row = 16 * (wave * TPW + i) + 4 * q + ii;
-                        cp[(size_t)row * DV + j0 + 16 * ct + m] = S[i][ct][ii];
-                    }
-        }
-        cur = nxt;
-    }
-
-    if (sfinal) {
-#pragma unroll
-        for (int i = 0; i < TPW; ++i)
+            const bool valid = vs < len;
 #pragma unroll
             for (int ct = 0; ct < NT; ++ct)
 #pragma unroll
-                for (int ii = 0; ii < 4; ++ii) {
-                    const int row = 16 * (wave * TPW + i) + 4 * q + ii;
-                    sfinal[sbase + (size_t)row * DV + j0 + 16 * ct + m] = S[i][ct][ii];
+                for (int cc = 0; cc < 4; ++cc) {
+                    float val;
+                    if constexpr (BF16) val = bf16_to_f32(cur.v[ct][cc]);
+                    else val = cur.v[ct][cc];
+                    sV[ts][ct][vc + cc + 16 * qq][ee] = (E)(valid ? val : 0.f);
                 }
+        }
+        __syncthreads();
+
+        // (c) U = Ab V - W S ; O^T = S^T Qd^T  (row tile = wave). A B-operand
+        // fragment of X (K x N) is also the A-operand fragment of X^T, so O^T
+        // takes the same fragments with the operands swapped; its result tile
+        // gives each lane 4 adjacent value columns of one token (16-byte stores).
+        f32x4 U[NT], O[NT];
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct) {
+            U[ct] = M::run(cur.ab[0], *reinterpret_cast<const Frag*>(&sV[0][ct][lane][0]), f32x4{0.f, 0.f, 0.f, 0.f});
+            U[ct] = M::run(cur.ab[1], *reinterpret_cast<const Frag*>(&sV[1][ct][lane][0]), U[ct]);
+            O[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+            for (int ct = 0; ct < NT; ++ct) {
+                const Frag sf = *reinterpret_cast<const Frag*>(&sS[ks][ct][lane][0]);
+                U[ct] = M::run(cur.wn[ks], sf, U[ct]);
+                O[ct] = M::run(sf, cur.qd[ks], O[ct]);
+            }
+        // (d) publish U as B-frags (K = tokens): slab rt/2, half rt%2
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct) {
+            e4 u4;
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) u4[ii] = (E)U[ct][ii];
+            *reinterpret_cast<e4*>(&sU[rt / 2][ct][lane][4 * (rt % 2)]) = u4;
+        }
+        __syncthreads();
+
+        // (g) S <- diag(Gamma_last) S + Kc^T U  (on the dependency chain: first)
+#pragma unroll
+        for (int i = 0; i < TPW; ++i)
+#pragma unroll
+            for (int ct = 0; ct < NT; ++ct) {
+                f32x4 a = S[i][ct] * cur.gl[i];
+                a = M::run(cur.kc[i][0], *reinterpret_cast<const Frag*>(&sU[0][ct][lane][0]), a);
+                a = M::run(cur.kc[i][1], *reinterpret_cast<const Frag*>(&sU[1][ct][lane][0]), a);
+                S[i][ct] = a;
+            }
+
+        // (f) O^T += U^T P^T; lane (m, q) holds token 16*rt + m, columns 4q .. 4q+3
+        // of each 16-column tile: one 16-byte store per tile (a token past the
+        // end of the sequence stores to the sink)
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct) {
+            O[ct] = M::run(*reinterpret_cast<const Frag*>(&sU[0][ct][lane][0]), cur.p[0], O[ct]);
+            O[ct] = M::run(*reinterpret_cast<const Frag*>(&sU[1][ct][lane][0]), cur.p[1], O[ct]);
+        }
+        {
+            const int tok = 16 * rt + m;
+            float* op = tok < len ? o + ((tok0 + tok) * H + h) * (int64_t)DV + j0 + 4 * q : my_sink;
+#pragma unroll
+            for (int ct = 0; ct < NT; ++ct)
+                *reinterpret_cast<f32x4*>(op + (tok < len ? 16 * ct : 0)) = O[ct];
+        }
+
+    };
+
+    // Chunks run in segments that end on checkpoint boundaries, so the
+    // branch-free chunk loop never stores a state; each checkpoint is written
+    // between segments. Without checkpoints there is one segment.
+    const int ick = interval > 0 ? (int)(interval / C) : nch;  // chunks per segment
+    int64_t cidx = cpbase;
+    Ops b0, b1, b2;
+    for (int seg0 = 0; seg0 < nch; seg0 += ick) {
+        const int seg1 = seg0 + ick < nch ? seg0 + ick : nch;
+        load_ops(b0, seg0);
+        load_ops(b1, seg0 + 1 < seg1 ? seg0 + 1 : seg0);
+        for (int n = seg0; n < seg1; n += 3) {
+            load_ops(b2, n + 2 < seg1 ? n + 2 : seg1 - 1);
+            step(b0, n);
+            if (n + 1 >= seg1) break;
+            load_ops(b0, n + 3 < seg1 ? n + 3 : seg1 - 1);
+            step(b1, n + 1);
+            if (n + 2 >= seg1) break;
+            load_ops(b1, n + 4 < seg1 ? n + 4 : seg1 - 1);
+            step(b2, n + 2);
+        }
+        // a full segment ends exactly ick * 64 tokens later: checkpoint
+        if (interval > 0 && (int64_t)seg1 * C <= L && seg1 - seg0 == ick) {
+            if (cidx < ckpt_rows) store_state(ckpt + (cidx * H + h) * (size_t)DK * DV);
+            ++cidx;
+        }
     }
+
+    if (sfinal) store_state(sfinal + sbase);
 }
 
 // ------------------------------------------------------------- host side ---
@@ -882,6 +903,7 @@ struct Plan {
     int32_t* ckpt_base;
     int32_t* order;
     unsigned char* handoff;
+    float* sink;
     int64_t max_chunks;
 };
 
@@ -892,8 +914,22 @@ Plan make_plan(const PrefillArgs& a) {
     p.ckpt_base = p.chunk_start + (a.num_seqs + 1);
     p.order = p.ckpt_base + (a.num_seqs + 1);
     p.handoff = ws + table_bytes(a.num_seqs);
+    p.sink = reinterpret_cast<float*>(p.handoff - kSinkBytes);
     p.max_chunks = max_chunks(a.total_tokens, a.num_seqs);
     return p;
+}
+
+template <int DK, int DV, int NT, bool BF16>
+void launch_scan(const PrefillArgs& a, const Plan& p, int npairs, hipStream_t stream) {
+    constexpr int NVB = DV / (16 * NT);
+    const bool varlen = a.cu_seqlens != nullptr;
+    const int64_t groups = (npairs + 7) / 8;
+    const unsigned grid = (unsigned)(groups * 8 * NVB);
+    hipLaunchKernelGGL((k2_scan_kernel<DK, DV, NT, BF16>), dim3(grid), dim3(kThreads), 0, stream,
+                       a.v, a.cu_seqlens, varlen ? p.order : nullptr,
+                       varlen ? p.chunk_start : nullptr, varlen ? p.ckpt_base : nullptr, npairs,
+                       a.total_tokens, a.H, p.max_chunks, p.handoff, a.initial_state, a.final_state,
+                       a.ckpt_interval, a.ckpt_states, a.ckpt_rows, a.o, p.sink);
 }
 
 template <int DK, int DV, bool BF16>
@@ -909,17 +945,42 @@ hipError_t launch_typed(const PrefillArgs& a, hipStream_t stream) {
                            dim3(kThreads), 0, stream, a.q, a.k, a.g, a.beta, a.cu_seqlens,
                            varlen ? p.chunk_start : nullptr, a.num_seqs, a.total_tokens, a.H,
                            p.max_chunks, p.handoff);
-    constexpr int NT = 1;
-    constexpr int NVB = DV / (16 * NT);
+    // Value columns per scan workgroup. Every workgroup streams the whole
+    // handoff of its (sequence, head) through its CU, so wider column blocks
+    // cost fewer bytes per column but more serial work per chunk. Measured
+    // chunk-step times on MI355X for 16, 32 and 64 columns: about 1.73, 2.11
+    // and 3.08 us. Pick the width with the least (rounds of workgroups over the
+    // CUs) x (step time); fp32 operands are twice as wide, so that path keeps 16.
     const int npairs = a.num_seqs * a.H;
-    const int64_t groups = (npairs + 7) / 8;
-    const unsigned grid = (unsigned)(groups * 8 * NVB);
-    if (scan)
-        hipLaunchKernelGGL((k2_scan_kernel<DK, DV, NT, BF16>), dim3(grid), dim3(kThreads), 0, stream,
-                       a.v, a.cu_seqlens, varlen ? p.order : nullptr,
-                       varlen ? p.chunk_start : nullptr, varlen ? p.ckpt_base : nullptr, npairs,
-                       a.total_tokens, a.H, p.max_chunks, p.handoff, a.initial_state, a.final_state,
-                       a.ckpt_interval, a.ckpt_states, a.ckpt_rows, a.o);
+    int cus = 256;
+    {
+        int dev = 0;
+        if (hipGetDevice(&dev) == hipSuccess) {
+            int n = 0;
+            if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+                cus = n;
+        }
+    }
+    int nt = 1;
+    if (BF16) {
+        const int64_t step_cost[3] = {173, 211, 308};
+        int64_t best = -1;
+        for (int li = 0; li < 3; ++li) {
+            const int cand = 1 << li;
+            if (DV % (16 * cand) != 0) continue;
+            const int64_t wgs = (int64_t)npairs * (DV / (16 * cand));
+            const int64_t cost = (wgs + cus - 1) / cus * step_cost[li];
+            if (best < 0 || cost < best) {
+                best = cost;
+                nt = cand;
+            }
+        }
+    }
+    if (scan) {
+        if (nt == 4) launch_scan<DK, DV, 4, BF16>(a, p, npairs, stream);
+        else if (nt == 2) launch_scan<DK, DV, 2, BF16>(a, p, npairs, stream);
+        else launch_scan<DK, DV, 1, BF16>(a, p, npairs, stream);
+    }
     return hipGetLastError();
 }
 

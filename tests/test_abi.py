@@ -47,9 +47,10 @@ def ws_size(N=8192, S=1, H=32, Dk=128, Dv=128, chunk=64, dt=B.KDA_BF16):
 def test_workspace_size():
     per_chunk_bf16 = (192 * 128 + 8192) * 2 + 4 * 128
     assert per_chunk_bf16 == 66048
-    assert ws_size() == 256 + 32 * (8192 // 64 + 1) * per_chunk_bf16
+    table = 256 + 64 * 256 * 8 * 4  # sequence tables + store sink
+    assert ws_size() == table + 32 * (8192 // 64 + 1) * per_chunk_bf16
     per_chunk_f32 = (192 * 64 + 8192) * 4 + 4 * 64
-    assert ws_size(256, 1, 2, 64, 64, 64, B.KDA_F32) == 256 + 2 * 5 * per_chunk_f32
+    assert ws_size(256, 1, 2, 64, 64, 64, B.KDA_F32) == table + 2 * 5 * per_chunk_f32
     assert ws_size(Dk=96) == 0
     assert ws_size(chunk=32) == 0
     assert ws_size(N=-1) == 0
