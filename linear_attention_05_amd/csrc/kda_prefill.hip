@@ -266,7 +266,7 @@ __device__ __forceinline__ void locate_chunk(int ci, const int32_t* cu, const in
 //           row's inner sum, two lane exchanges combine them
 //   W       -W = -Ainv diag(beta) Kd via MFMA on W^T tiles; Ab = Ainv diag(beta)
 template <int DK, bool BF16>
-__global__ __launch_bounds__(kThreads) void k1_prep_kernel(
+__global__ __launch_bounds__(kThreads, BF16 ? 3 : 2) void k1_prep_kernel(
     const void* __restrict__ qin, const void* __restrict__ kin, const float* __restrict__ g,
     const float* __restrict__ beta, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ chunk_start, int num_seqs, int64_t N, int H, int64_t max_chunks,
@@ -286,11 +286,16 @@ __global__ __launch_bounds__(kThreads) void k1_prep_kernel(
     constexpr int RPQ = C / NQ;
     typedef TIn tin8 __attribute__((ext_vector_type(8)));
 
-    __shared__ __attribute__((aligned(16))) TIn sK[C][KP];
+    // K is dead once phase A has built every operand that needs it, so A and
+    // then Ainv reuse its LDS (K1 fits three workgroups per CU this way).
+    constexpr int KBYTES = C * KP * (int)sizeof(TIn);
+    constexpr int ABYTES = C * AP * (int)sizeof(float);
+    __shared__ __attribute__((aligned(16))) unsigned char sKA[KBYTES > ABYTES ? KBYTES : ABYTES];
     __shared__ __attribute__((aligned(16))) float sG[C][GP];  // g, then G * log2(e)
-    __shared__ __attribute__((aligned(16))) float sA[C][AP];  // A, then Ainv
     __shared__ float sB[C];
     __shared__ double sTot[NQ][DK];
+    TIn(*sK)[KP] = reinterpret_cast<TIn(*)[KP]>(sKA);
+    float(*sA)[AP] = reinterpret_cast<float(*)[AP]>(sKA);
 
     const int ci = blockIdx.x;
     const int h = blockIdx.y;
@@ -332,9 +337,8 @@ __global__ __launch_bounds__(kThreads) void k1_prep_kernel(
     }
     const float breg = (t < C && t < len) ? beta[(t0 + t) * H + h] : 0.f;
 
-    // q values this wave needs later, prefetched now:
-    //   qa[gi][ks]: row 16*rb + m, channels 32ks + 8q .. +7 of the wave's row blocks
-    //   qd[i][0|1]: Qd handoff frag f = wave + 4i, channels 32ks + 4q .. +3 and + 16
+    // q values of the wave's phase-A row blocks, prefetched now:
+    //   qa[gi][ks]: row 16*rb + m, channels 32ks + 8q .. +7
     typedef TIn tin8 __attribute__((ext_vector_type(8)));
     typedef TIn tin4 __attribute__((ext_vector_type(4)));
     const int plan[4][2][3] = {{{3, 0, 2}, {0, 0, 1}},   // {rb, sb_first, count}
@@ -351,16 +355,6 @@ __global__ __launch_bounds__(kThreads) void k1_prep_kernel(
             qa[gi][ks] = (rb >= 0 && r < len) ? *reinterpret_cast<const tin8*>(Q + row_off(r) + 32 * ks + 8 * q) : tin8{};
     }
     constexpr int QDF = 4 * NKS / 4;  // Qd frags per wave
-    tin4 qd[QDF][2];
-#pragma unroll
-    for (int i = 0; i < QDF; ++i) {
-        const int f = wave + 4 * i;
-        const int rt = f / NKS, ks = f % NKS;
-        const int r = 16 * rt + m;
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-            qd[i][hh] = r < len ? *reinterpret_cast<const tin4*>(Q + row_off(r) + 32 * ks + 16 * hh + 4 * q) : tin4{};
-    }
 
 #pragma unroll
     for (int u = 0; u < KV; ++u) {
@@ -403,6 +397,21 @@ __global__ __launch_bounds__(kThreads) void k1_prep_kernel(
         else return v;
     };
 
+    f32x4 aT[4];  // A tiles of this wave's block pairs (slot 2*gi + k2)
+
+    // q values of this wave's Qd handoff frags (used at the end of phase A):
+    // frag f = wave + 4i, channels 32ks + 4q .. +3 and + 16
+    tin4 qd[QDF][2];
+#pragma unroll
+    for (int i = 0; i < QDF; ++i) {
+        const int f = wave + 4 * i;
+        const int rt = f / NKS, ks = f % NKS;
+        const int r = 16 * rt + m;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+            qd[i][hh] = r < len ? *reinterpret_cast<const tin4*>(Q + row_off(r) + 32 * ks + 16 * hh + 4 * q) : tin4{};
+    }
+
     // ---- phase A: 16x16 block pairs (rb, sb), sb <= rb, reference row 16*rb:
     // every factor e^(G_r - G_ref) (r >= ref) is <= 1 and e^(G_ref - G_s) is
     // <= 1 for s < ref. Waves take the pairs grouped by rb so the row-block
@@ -425,7 +434,9 @@ __global__ __launch_bounds__(kThreads) void k1_prep_kernel(
                     Z[ks][e] = (E)(qf(qa[gi][ks][e]) * fr);
                 }
             }
-            for (int k2 = 0; k2 < plan[wave][gi][2]; ++k2) {
+#pragma unroll
+            for (int k2 = 0; k2 < 2; ++k2) {
+                if (k2 >= plan[wave][gi][2]) break;
                 const int sb = plan[wave][gi][1] + k2;
                 const int s = 16 * sb + m;
                 f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
@@ -440,28 +451,30 @@ __global__ __launch_bounds__(kThreads) void k1_prep_kernel(
                     accA = M::run(X[ks], Y, accA);  // rows r, cols s
                     accP = M::run(Y, Z[ks], accP);  // P^T: rows s, cols r
                 }
-                // A[r'][s'] with r' = 16rb + 4q + i, s' = 16sb + m
+                // A[r'][s'] with r' = 16rb + 4q + i, s' = 16sb + m, kept in
+                // registers until every wave is done reading K
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int rr = 16 * rb + 4 * q + i, ss = 16 * sb + m;
-                    sA[rr][ss] = ss < rr ? sB[rr] * accA[i] : 0.f;
+                    aT[2 * gi + k2][i] = ss < rr ? sB[rr] * accA[i] : 0.f;
                 }
                 // P^T[s'][r'] with s' = 16sb + 4q + i, r' = 16rb + m -> P A-frag
                 // [rt = rb][slab sb/2], slots 4*(sb%2) + i of lane (m + 16q).
-                E* pf = hb + HO::kP + ((size_t)(rb * 2 + sb / 2) * 64 + lane) * 8 + 4 * (sb % 2);
+                typedef E e4 __attribute__((ext_vector_type(4)));
+                e4 pv;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int ss = 16 * sb + 4 * q + i, rr = 16 * rb + m;
-                    pf[i] = (E)(ss <= rr ? accP[i] : 0.f);
+                    pv[i] = (E)(ss <= rr ? accP[i] : 0.f);
                 }
+                *reinterpret_cast<e4*>(hb + HO::kP + ((size_t)(rb * 2 + sb / 2) * 64 + lane) * 8 + 4 * (sb % 2)) = pv;
             }
         }
         // zero halves inside stored slabs: (rb, sb) = (0, 1) and (2, 3)
         if (wave == 2 || wave == 3) {
             const int rb = wave == 2 ? 0 : 2, sb = rb + 1;
-            E* pf = hb + HO::kP + ((size_t)(rb * 2 + sb / 2) * 64 + lane) * 8 + 4 * (sb % 2);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) pf[i] = (E)0.f;
+            typedef E e4 __attribute__((ext_vector_type(4)));
+            *reinterpret_cast<e4*>(hb + HO::kP + ((size_t)(rb * 2 + sb / 2) * 64 + lane) * 8 + 4 * (sb % 2)) = e4{};
         }
         // whole zero slabs (row tiles 0-1, token slab 1) of P and Ab
         if (wave < 2) {
@@ -498,6 +511,38 @@ __global__ __launch_bounds__(kThreads) void k1_prep_kernel(
             store_frag<Frag, E>(hb + HO::kKc, ct * 2 + ts, lane, out);
         }
         for (int c = t; c < DK; c += kThreads) glast[c] = fast_exp2(sG[C - 1][c]);
+    }
+    // (beta Kd)^T operands of phase C, built while K is still in LDS:
+    // row c = 16(2ks + half) + m, K index s = 32ts + 8q + e, ks = wave % NKS
+    Frag aF[2][2];
+    {
+        const int ks = wave % NKS;
+#pragma unroll
+        for (int half = 0; half < 2; ++half)
+#pragma unroll
+            for (int ts = 0; ts < 2; ++ts) {
+                const int c = 16 * (2 * ks + half) + m;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int s = 32 * ts + 8 * q + e;
+                    aF[half][ts][e] = (E)(sB[s] * kval(s, c) * fast_exp2(sG[s][c]));
+                }
+            }
+    }
+    __syncthreads();
+
+    // K is no longer read: the A tiles go to its LDS
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi) {
+        const int rb = plan[wave][gi][0];
+        if (rb < 0) break;
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+            if (k2 >= plan[wave][gi][2]) break;
+            const int sb = plan[wave][gi][1] + k2;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sA[16 * rb + 4 * q + i][16 * sb + m] = aT[2 * gi + k2][i];
+        }
     }
     __syncthreads();
 
@@ -581,18 +626,6 @@ __global__ __launch_bounds__(kThreads) void k1_prep_kernel(
     // same rt stack into the W A-frag of (rt, slab ks). Each wave keeps one ks.
     {
         const int ks = wave % NKS;
-        Frag aF[2][2];  // (beta Kd)^T: row c = 16(2ks+half) + m, K = s = 32ts + 8q + e
-#pragma unroll
-        for (int half = 0; half < 2; ++half)
-#pragma unroll
-            for (int ts = 0; ts < 2; ++ts) {
-                const int c = 16 * (2 * ks + half) + m;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int s = 32 * ts + 8 * q + e;
-                    aF[half][ts][e] = (E)(sB[s] * kval(s, c) * fast_exp2(sG[s][c]));
-                }
-            }
         for (int f = wave; f < 4 * NKS; f += 4) {
             const int rt = f / NKS;
             f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
