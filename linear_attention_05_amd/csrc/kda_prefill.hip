@@ -750,32 +750,46 @@ __global__ __launch_bounds__(kThreads) void k2_scan_kernel(
     const unsigned char* hbase = handoff + ((size_t)h * max_chunks + cbase) * HO::kBytes;
 
     // Issue every load of chunk n (0 <= n < nch: in bounds).
-    auto load_ops = [&](Ops& op, int n) {
+    // Issue the loads of chunk n (0 <= n < nch: in bounds) in four groups, so a
+    // step can spread them over its phases instead of filling the memory
+    // queue in one burst (a wave issues in order: a full queue would stall
+    // its arithmetic behind its own prefetches).
+    auto load_ops = [&](Ops& op, int n, int grp) {
         const E* hb = reinterpret_cast<const E*>(hbase + (size_t)n * HO::kBytes);
-        const float* glast = reinterpret_cast<const float*>(reinterpret_cast<const unsigned char*>(hb) + HO::kGlastBytes);
+        if (grp == 0) {
 #pragma unroll
-        for (int ts = 0; ts < 2; ++ts) {
-            op.ab[ts] = load_frag<Frag, E>(hb + HO::kAb, rt * 2 + ts, lane);
-            op.p[ts] = load_frag<Frag, E>(hb + HO::kP, rt * 2 + ts, lane);
+            for (int ts = 0; ts < 2; ++ts) {
+                op.ab[ts] = load_frag<Frag, E>(hb + HO::kAb, rt * 2 + ts, lane);
+                op.p[ts] = load_frag<Frag, E>(hb + HO::kP, rt * 2 + ts, lane);
+            }
+        } else if (grp == 1) {
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) op.wn[ks] = load_frag<Frag, E>(hb + HO::kW, rt * NKS + ks, lane);
+        } else if (grp == 2) {
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) op.qd[ks] = load_frag<Frag, E>(hb + HO::kQd, rt * NKS + ks, lane);
+        } else {
+            const float* glast = reinterpret_cast<const float*>(reinterpret_cast<const unsigned char*>(hb) + HO::kGlastBytes);
+#pragma unroll
+            for (int i = 0; i < TPW; ++i) {
+                const int srt = wave * TPW + i;
+                op.kc[i][0] = load_frag<Frag, E>(hb + HO::kKc, srt * 2 + 0, lane);
+                op.kc[i][1] = load_frag<Frag, E>(hb + HO::kKc, srt * 2 + 1, lane);
+                op.gl[i] = *reinterpret_cast<const f32x4*>(glast + 16 * srt + 4 * q);
+            }
+            // token rows past the end read the last valid row (zeroed when staged)
+            const int64_t left = L - (int64_t)n * C;
+            const int64_t tok = tstart + (int64_t)n * C + (vs < left ? vs : left - 1);
+#pragma unroll
+            for (int ct = 0; ct < NT; ++ct)
+                op.v[ct] = *reinterpret_cast<const tin4*>(V + (tok * H + h) * (int64_t)DV + j0 + 16 * ct + vc);
         }
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            op.wn[ks] = load_frag<Frag, E>(hb + HO::kW, rt * NKS + ks, lane);
-            op.qd[ks] = load_frag<Frag, E>(hb + HO::kQd, rt * NKS + ks, lane);
-        }
-#pragma unroll
-        for (int i = 0; i < TPW; ++i) {
-            const int srt = wave * TPW + i;
-            op.kc[i][0] = load_frag<Frag, E>(hb + HO::kKc, srt * 2 + 0, lane);
-            op.kc[i][1] = load_frag<Frag, E>(hb + HO::kKc, srt * 2 + 1, lane);
-            op.gl[i] = *reinterpret_cast<const f32x4*>(glast + 16 * srt + 4 * q);
-        }
-        // token rows past the end read the last valid row (zeroed when staged)
-        const int64_t left = L - (int64_t)n * C;
-        const int64_t tok = tstart + (int64_t)n * C + (vs < left ? vs : left - 1);
-#pragma unroll
-        for (int ct = 0; ct < NT; ++ct)
-            op.v[ct] = *reinterpret_cast<const tin4*>(V + (tok * H + h) * (int64_t)DV + j0 + 16 * ct + vc);
+    };
+    auto load_all = [&](Ops& op, int n) {
+        load_ops(op, n, 0);
+        load_ops(op, n, 1);
+        load_ops(op, n, 2);
+        load_ops(op, n, 3);
     };
 
     // state rows owned: channel 16*srt + 4q + i, column j0 + 16ct + m
@@ -806,8 +820,9 @@ __global__ __launch_bounds__(kThreads) void k2_scan_kernel(
                     dst[(size_t)(16 * (wave * TPW + i) + 4 * q + ii) * DV + j0 + 16 * ct + m] = S[i][ct][ii];
     };
 
-    // One chunk step with operands `cur` (chunk n).
-    auto step = [&](const Ops& cur, int n) {
+    // One chunk step with operands `cur` (chunk n), prefetching chunk `pn` into `nxt`.
+    auto step = [&](const Ops& cur, int n, Ops& nxt, int pn) {
+        load_ops(nxt, pn, 0);
         const int64_t tok0 = tstart + (int64_t)n * C;
         const int64_t left = L - (int64_t)n * C;
         const int len = left < C ? (int)left : C;
@@ -841,6 +856,9 @@ __global__ __launch_bounds__(kThreads) void k2_scan_kernel(
                 }
         }
         __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+        load_ops(nxt, pn, 1);
+        __builtin_amdgcn_sched_barrier(0);
 
         // (c) U = Ab V - W S ; O^T = S^T Qd^T  (row tile = wave). A B-operand
         // fragment of X (K x N) is also the A-operand fragment of X^T, so O^T
@@ -869,7 +887,13 @@ __global__ __launch_bounds__(kThreads) void k2_scan_kernel(
             for (int ii = 0; ii < 4; ++ii) u4[ii] = (E)U[ct][ii];
             *reinterpret_cast<e4*>(&sU[rt / 2][ct][lane][4 * (rt % 2)]) = u4;
         }
+        __builtin_amdgcn_sched_barrier(0);
+        load_ops(nxt, pn, 2);
+        __builtin_amdgcn_sched_barrier(0);
         __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+        load_ops(nxt, pn, 3);
+        __builtin_amdgcn_sched_barrier(0);
 
         // (g) S <- diag(Gamma_last) S + Kc^T U  (on the dependency chain: first)
 #pragma unroll
@@ -908,17 +932,14 @@ __global__ __launch_bounds__(kThreads) void k2_scan_kernel(
     Ops b0, b1, b2;
     for (int seg0 = 0; seg0 < nch; seg0 += ick) {
         const int seg1 = seg0 + ick < nch ? seg0 + ick : nch;
-        load_ops(b0, seg0);
-        load_ops(b1, seg0 + 1 < seg1 ? seg0 + 1 : seg0);
+        load_all(b0, seg0);
+        load_all(b1, seg0 + 1 < seg1 ? seg0 + 1 : seg0);
         for (int n = seg0; n < seg1; n += 3) {
-            load_ops(b2, n + 2 < seg1 ? n + 2 : seg1 - 1);
-            step(b0, n);
+            step(b0, n, b2, n + 2 < seg1 ? n + 2 : seg1 - 1);
             if (n + 1 >= seg1) break;
-            load_ops(b0, n + 3 < seg1 ? n + 3 : seg1 - 1);
-            step(b1, n + 1);
+            step(b1, n + 1, b0, n + 3 < seg1 ? n + 3 : seg1 - 1);
             if (n + 2 >= seg1) break;
-            load_ops(b1, n + 4 < seg1 ? n + 4 : seg1 - 1);
-            step(b2, n + 2);
+            step(b2, n + 2, b1, n + 4 < seg1 ? n + 4 : seg1 - 1);
         }
         // a full segment ends exactly ick * 64 tokens later: checkpoint
         if (interval > 0 && (int64_t)seg1 * C <= L && seg1 - seg0 == ick) {
