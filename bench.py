@@ -172,6 +172,75 @@ def cpu_baseline(x, target_s=10.0):
                 seconds=spent)
 
 
+def bench_prefill_workload(idx, reps=3):
+    """Time one whole prefill call of another workload (long-context with
+    checkpoints, or packed varlen): median over reps, inputs resident."""
+    import numpy as np
+    import torch
+    import linear_attention_05_amd as K
+    from linear_attention_05_amd import accounting as acc
+    from synth import make_workload
+
+    x = make_workload(idx)
+    N, H, D = x.total_tokens, x.H, x.Dk
+    args = [dev(a) for a in (x.q, x.k, x.v, x.g, x.beta)]
+    cu = dev(x.cu_seqlens)
+    s0 = dev(x.initial_state) if x.initial_state is not None else None
+    o = torch.empty(N, H, D, device="cuda")
+    fs = torch.empty(x.num_seqs, H, D, D, device="cuda")
+    nck = x.num_checkpoints()
+    ck = torch.empty(max(nck, 0), H, D, D, device="cuda") if x.ckpt_interval else None
+    ws = torch.empty(K.kda_prefill_workspace_size(N, x.num_seqs, H, D, D), dtype=torch.uint8,
+                     device="cuda")
+
+    def run():
+        K.kda_prefill_chunked(*args, cu_seqlens=cu, initial_state=s0, final_state=fs,
+                              ckpt_interval=x.ckpt_interval, ckpt_states=ck, o=o, workspace=ws)
+
+    run()
+    times = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        run()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    ms = float(np.median(times))
+    n_state = (x.num_seqs if x.initial_state is not None else 0) + x.num_seqs + nck
+    byts = acc.prefill_compulsory_bytes(N, H, D, D, 2, 0, 0) + n_state * H * D * D * 4
+    return dict(workload=x.name, tokens=N, seqs=x.num_seqs, ms=round(ms, 4),
+                mtok_s=round(N / (ms * 1e-3) / 1e6, 3),
+                tflops_algorithmic=round(N * H * acc.prefill_flops_per_token_head(D, D) / (ms * 1e-3) / 1e12, 2),
+                path_roofline_frac=round(byts / (ms * 1e-3) / 8e12, 4))
+
+
+def hbm_ceilings():
+    """Practical HBM rates of plain torch kernels on 1 GiB (context for the
+    roofline fractions): read-only (sum), write-only (fill), copy (read+write)."""
+    import torch
+    n = (1 << 30) // 4
+    a = torch.ones(n, device="cuda")
+    b = torch.empty_like(a)
+    out = {}
+    for name, fn, moved in (("read_sum", lambda: a.sum(), 1 << 30),
+                            ("write_fill", lambda: b.fill_(2.0), 1 << 30),
+                            ("copy", lambda: b.copy_(a), 2 << 30)):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        out[name + "_gbps"] = round(moved / (e0.elapsed_time(e1) / 10 * 1e-3) / 1e9, 1)
+    del a, b
+    return out
+
+
 def roofline(bytes_, ms, traffic=None):
     gbps = bytes_ / (ms * 1e-3) / 1e9
     return {"bound": "hbm", "achieved": round(gbps, 1), "peak": 8000.0, "unit": "GB/s",
@@ -186,6 +255,8 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=64)
     ap.add_argument("--only", choices=["all", "prefill", "decode"], default="all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra-workloads", action="store_true",
+                    help="skip timing the long-context and varlen prefill workloads")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run one device-to-device copy of this many MiB (a known-size "
                          "reference dispatch for hardware traffic counters)")
@@ -259,6 +330,9 @@ def main():
                         "dtype": "bf16 in; f32 state", "data": "synthetic",
                         "config": {"workload": out["decode"]["workload"]},
                         "roofline": out["decode"]["roofline"]})
+    if args.only == "all" and not args.no_extra_workloads:
+        out["prefill_workloads"] = [bench_prefill_workload(2), bench_prefill_workload(3)]
+        out["hbm_ceilings"] = hbm_ceilings()
     if args.only in ("all", "prefill") and not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(p["inputs"])
         out["cpu_baseline"]["seconds"] = round(out["cpu_baseline"]["seconds"], 2)
