@@ -330,8 +330,9 @@ def main():
                         "dtype": "bf16 in; f32 state", "data": "synthetic",
                         "config": {"workload": out["decode"]["workload"]},
                         "roofline": out["decode"]["roofline"]})
-    if args.only == "all" and not args.no_extra_workloads:
+    if args.only in ("all", "prefill") and not args.no_extra_workloads:
         out["prefill_workloads"] = [bench_prefill_workload(2), bench_prefill_workload(3)]
+    if args.only == "all" and not args.no_extra_workloads:
         out["hbm_ceilings"] = hbm_ceilings()
     if args.only in ("all", "prefill") and not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(p["inputs"])

@@ -29,8 +29,12 @@ def hipcc() -> str:
 
 
 def common_flags():
+    # -packed-fp32-ops: no packed fp32 instructions in generated code.
+    # -amdgpu-mfma-vgpr-form: matrix-core results in ordinary VGPRs, so the
+    # scan's state takes part in vector arithmetic without register copies.
     return ["-std=c++17", "-O3", "-fPIC", f"--offload-arch={ARCH}",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-mllvm", "-amdgpu-mfma-vgpr-form=1",
             "-Wall", "-Wno-unused-function", "-I", INCLUDE, "-I", CSRC]
 
 

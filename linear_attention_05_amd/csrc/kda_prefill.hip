@@ -20,8 +20,8 @@
 // Numerics. The state S and every accumulation are fp32; A, its inverse and
 // the decay exponents are fp32. With bf16 q/k/v the MFMA operands are fp16
 // (one pass of v_mfma_f32_16x16x32_f16; fp16 keeps 11 significant bits, 8x
-// finer than bf16, at the same matrix-core rate), and S enters W S and Qd S as
-// an fp16 hi/lo pair. With fp32 q/k/v every product runs on
+// finer than bf16, at the same matrix-core rate), S and U entering their
+// products rounded to fp16 once. With fp32 q/k/v every product runs on
 // v_mfma_f32_16x16x4_f32 with fp32 operands. Decay factors are formed as
 // e^(G_r - G_ref) with a reference row per 16-row block, so the products
 // never form e^(+G) of a whole chunk.
@@ -54,6 +54,7 @@ typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
 constexpr int C = kChunk;      // 64 tokens per chunk
 constexpr int kThreads = 256;  // 4 waves
 constexpr float kLog2e = 1.4426950408889634f;
+
 
 __device__ __forceinline__ float bf16_to_f32(unsigned short b) {
     return __uint_as_float(static_cast<unsigned>(b) << 16);
@@ -297,8 +298,11 @@ __global__ __launch_bounds__(kThreads, BF16 ? 3 : 2) void k1_prep_kernel(
     TIn(*sK)[KP] = reinterpret_cast<TIn(*)[KP]>(sKA);
     float(*sA)[AP] = reinterpret_cast<float(*)[AP]>(sKA);
 
-    const int ci = blockIdx.x;
-    const int h = blockIdx.y;
+    // Chunk-major, last chunk first, heads fastest: neighbouring workgroups
+    // read neighbouring rows of q, k and g, and the blocks the scan needs first
+    // are written last (likeliest to still be cached when it reads them).
+    const int h = (int)(blockIdx.x % (unsigned)H);
+    const int ci = (int)(max_chunks - 1 - (int64_t)(blockIdx.x / (unsigned)H));
     int64_t t0;
     int len;
     locate_chunk(ci, cu, chunk_start, num_seqs, N, t0, len);
@@ -951,6 +955,788 @@ __global__ __launch_bounds__(kThreads) void k2_scan_kernel(
     if (sfinal) store_state(sfinal + sbase);
 }
 
+// Three-wave scan: one workgroup = one (sequence, head) and 16 value columns,
+// with the whole state slice (DK x 16) in the registers of wave 0.
+//   wave 0  the chain: U = U0 - W S, then S <- diag(Gamma_last) S + Kc^T U.
+//           S and U pass from one product to the next inside the lane that
+//           holds them (the K-slab permutation): no LDS round trip.
+//   wave 1  runs two chunks ahead: stages a chunk's V tile, forms U0 = Ab V
+//           and Gamma_last for wave 0 (which reads them one step ahead, so no
+//           LDS latency sits on the chain), and touches the lines of the chunk
+//           five steps ahead so that the operand loads of all waves hit L2.
+//   wave 2  trails by one chunk: O^T = S^T Qd^T + U^T P^T from the S and U
+//           fragments wave 0 leaves in LDS, one 16-byte store per lane.
+// One barrier per chunk; the S/U fragments are double-buffered by chunk
+// parity, U0 and Gamma_last triple-buffered by chunk index mod 3. Register operands are reloaded for the next chunk right
+// after their last use. Vector memory counters complete in issue order, so
+// each wave issues its loads in the same order in the prologue as in the loop
+// and never waits on a load younger than about one chunk step. The V and
+// handoff pointers are not __restrict__: that keeps the compiler from moving
+// prefetches across the barriers. Blocks of Ab and P above the diagonal
+// (token rows 0-31, token slab 32-63) are zero and are neither loaded nor
+// multiplied.
+template <int DK, int DV, int NCB>
+__global__ __launch_bounds__(192 * NCB) __attribute__((amdgpu_waves_per_eu(1, 2))) void k2_trio_kernel(
+    const void* vin, const int32_t* __restrict__ cu, const int32_t* __restrict__ order,
+    const int32_t* __restrict__ chunk_start, const int32_t* __restrict__ ckpt_base, int npairs,
+    int64_t N, int H, int64_t max_chunks, const unsigned char* handoff,
+    const float* __restrict__ s0, float* __restrict__ sfinal, int64_t interval,
+    float* __restrict__ ckpt, int64_t ckpt_rows, float* __restrict__ o, float* __restrict__ sink) {
+    using M = Mma<true>;
+    using E = _Float16;
+    using Frag = half8;
+    using HO = Handoff<DK, true>;
+    typedef unsigned short us8 __attribute__((ext_vector_type(8)));
+    constexpr int NKS = DK / 32;  // K slabs over channels
+    constexpr int NST = DK / 16;  // state row tiles
+    constexpr int NRT = C / 16;   // token row tiles
+    constexpr int NVB = DV / 16;  // column blocks per (seq, head)
+    constexpr int kLines = (int)(HO::kBytes / 128);        // 128-byte lines per handoff block
+    constexpr int kLinesWg = (kLines + NVB - 1) / NVB;     // lines each column block touches
+    constexpr int NTH = (kLinesWg + 63) / 64;              // handoff touches per lane
+
+    constexpr int NWG = NVB / NCB;  // workgroups per (seq, head)
+    static_assert(NVB % NCB == 0, "column blocks split evenly over workgroups");
+
+    // one set per column block of the workgroup
+    __shared__ __attribute__((aligned(16))) E sVs[NCB][2][64][8];            // V tile B-frags [slab]
+    __shared__ __attribute__((aligned(16))) f32x4 sU0s[NCB][3][NRT][64];      // U0 = Ab V (result layout)
+    __shared__ __attribute__((aligned(16))) float sGs[NCB][3][DK];            // Gamma_last
+    __shared__ __attribute__((aligned(16))) E sSUs[NCB][2][NKS + 2][64][8];   // S(n) then U(n) fragments
+
+    // wave roles: waves 0..NCB-1 run the chains (one SIMD each), then the
+    // output waves, then the preparation waves; cb = column block in the group
+    const int wave = threadIdx.x >> 6;
+    const int role = wave / NCB, cb = wave % NCB;
+    auto& sV = sVs[cb];
+    auto& sU0 = sU0s[cb];
+    auto& sG = sGs[cb];
+    auto& sSU = sSUs[cb];
+
+    const int id = blockIdx.x;
+    const int xcd = id & 7, slot = id >> 3;
+    const int pair = xcd + 8 * (slot / NWG);
+    const int vb = (slot % NWG) * NCB + cb;
+    if (pair >= npairs) return;
+    const int rank = pair / H, h = pair % H;
+    const int seq = order ? order[rank] : rank;
+    int64_t tstart = 0, L = N;
+    if (cu) seq_range(cu, seq, N, tstart, L);
+    const int cbase = chunk_start ? chunk_start[seq] : 0;
+    int nch = (int)((L + C - 1) / C);
+    if (cbase + (int64_t)nch > max_chunks) nch = cbase < max_chunks ? (int)(max_chunks - cbase) : 0;
+    const int j0 = vb * 16;
+    const int last = nch > 0 ? nch - 1 : 0;
+    auto clampc = [&](int n) { return n < last ? n : last; };
+
+    const int lane = threadIdx.x & 63;
+    const int q = lane >> 4;
+    const int m = lane & 15;
+    const unsigned char* hbase = handoff + ((size_t)h * max_chunks + cbase) * HO::kBytes;
+    auto hptr = [&](int n) { return reinterpret_cast<const E*>(hbase + (size_t)n * HO::kBytes); };
+    auto chunk_len = [&](int n) {
+        const int64_t left = L - (int64_t)n * C;
+        return left < C ? (int)left : C;
+    };
+    const unsigned short* V = static_cast<const unsigned short*>(vin);
+    // this lane's V row of chunk n (rows past the end repeat the last valid row)
+    auto vrow = [&](int n) {
+        const int64_t left = L - (int64_t)n * C;
+        const int64_t tok = tstart + (int64_t)n * C + (lane < left ? lane : left - 1);
+        return V + (tok * H + h) * (int64_t)DV + j0;
+    };
+
+    if (role == 0) {
+        // ------------------------------------------------------ the chain ----
+        Frag wn[NRT][NKS], kc[NST][2];
+        auto load_w = [&](int n) {
+            const E* hb = hptr(n);
+#pragma unroll
+            for (int r = 0; r < NRT; ++r)
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) wn[r][ks] = load_frag<Frag, E>(hb + HO::kW, r * NKS + ks, lane);
+        };
+        auto load_k = [&](int n) {
+            const E* hb = hptr(n);
+#pragma unroll
+            for (int i = 0; i < NST; ++i) {
+                kc[i][0] = load_frag<Frag, E>(hb + HO::kKc, i * 2 + 0, lane);
+                kc[i][1] = load_frag<Frag, E>(hb + HO::kKc, i * 2 + 1, lane);
+            }
+        };
+        // state rows owned: channel 16 i + 4 q + ii, column j0 + m
+        f32x4 S[NST];
+        const size_t sbase = ((size_t)seq * H + h) * DK * DV;
+        if (s0) {
+#pragma unroll
+            for (int i = 0; i < NST; ++i)
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) S[i][ii] = s0[sbase + (size_t)(16 * i + 4 * q + ii) * DV + j0 + m];
+        } else {
+#pragma unroll
+            for (int i = 0; i < NST; ++i) S[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        auto store_state = [&](float* dst) {
+#pragma unroll
+            for (int i = 0; i < NST; ++i)
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) dst[(size_t)(16 * i + 4 * q + ii) * DV + j0 + m] = S[i][ii];
+        };
+        // U0 (result layout) and Gamma_last rows of a chunk, read from LDS one
+        // step ahead (wave 1 writes chunk n + 2 while wave 0 runs chunk n)
+        f32x4 u0[NRT], gl[NST];
+        auto read_prep = [&](int n) {
+            const int b = n % 3;
+#pragma unroll
+            for (int r = 0; r < NRT; ++r) u0[r] = sU0[b][r][lane];
+#pragma unroll
+            for (int i = 0; i < NST; ++i) gl[i] = *reinterpret_cast<const f32x4*>(&sG[b][16 * i + 4 * q]);
+        };
+        auto step = [&](int n, int pn) {
+            const int par = n & 1;
+            // U = U0 - W S, slab by slab as S converts; S <- Gamma S meanwhile
+            Frag sf[NKS];
+            f32x4 U[NRT];
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) {
+                    sf[ks][ii] = (E)S[2 * ks][ii];
+                    sf[ks][4 + ii] = (E)S[2 * ks + 1][ii];
+                }
+#pragma unroll
+                for (int r = 0; r < NRT; ++r) U[r] = M::run(wn[r][ks], sf[ks], ks == 0 ? u0[r] : U[r]);
+            }
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) *reinterpret_cast<Frag*>(&sSU[par][ks][lane][0]) = sf[ks];
+#pragma unroll
+            for (int i = 0; i < NST; ++i) S[i] = S[i] * gl[i];
+            __builtin_amdgcn_sched_barrier(0);
+            load_w(pn);
+            read_prep(n + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            Frag uf[2];
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) {
+                    uf[s][ii] = (E)U[2 * s][ii];
+                    uf[s][4 + ii] = (E)U[2 * s + 1][ii];
+                }
+                *reinterpret_cast<Frag*>(&sSU[par][NKS + s][lane][0]) = uf[s];
+            }
+            // S <- diag(Gamma_last) S + Kc^T U
+#pragma unroll
+            for (int i = 0; i < NST; ++i) {
+                const f32x4 a = M::run(kc[i][0], uf[0], S[i]);
+                S[i] = M::run(kc[i][1], uf[1], a);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            load_k(pn);
+            __builtin_amdgcn_sched_barrier(0);
+            __syncthreads();
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        load_w(0);
+        load_k(0);
+        __syncthreads();  // U0 and Gamma of chunks 0 and 1 ready
+        __builtin_amdgcn_sched_barrier(0);
+        read_prep(0);
+        // Drain the prologue's loads: the compiler orders them freely, and the
+        // loop's memory waits must only reflect the loop's own issue order.
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        // Chunks run in segments that end on checkpoint boundaries, so the
+        // chunk loop itself never branches; each checkpoint is stored between
+        // segments. Without checkpoints there is one segment.
+        const int ick = interval > 0 ? (int)(interval / C) : (nch > 0 ? nch : 1);
+        int64_t cidx = ckpt_base ? ckpt_base[seq] : 0;
+        for (int seg0 = 0; seg0 < nch; seg0 += ick) {
+            const int seg1 = seg0 + ick < nch ? seg0 + ick : nch;
+            for (int n = seg0; n < seg1; ++n) step(n, clampc(n + 1));
+            if (interval > 0 && (int64_t)seg1 * C <= L && seg1 - seg0 == ick) {
+                if (cidx < ckpt_rows) store_state(ckpt + (cidx * H + h) * (size_t)DK * DV);
+                ++cidx;
+                // drain the checkpoint stores here, so that the chunk loop's
+                // memory waits need not allow for them (they are rare)
+                __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+            }
+        }
+        if (sfinal) store_state(sfinal + sbase);
+    } else if (role == 2) {
+        // ------------------------------------------ next-chunk preparation ----
+        // V staging: this lane's token -> slab, B-frag lane group and slot (inverse of perm32)
+        const int vslab = lane >> 5, w32 = lane & 31;
+        const int vq = (w32 & 15) >> 2, ve = (w32 & 3) + ((w32 >> 4) << 2);
+        const int glane = lane < DK / 4 ? lane : 0;  // Gamma_last: lane holds channels 4l..4l+3
+        int tline[NTH];  // this lane's lines of a handoff block (clamped into the block)
+#pragma unroll
+        for (int k = 0; k < NTH; ++k) {
+            const int t = vb * kLinesWg + (lane + 64 * k < kLinesWg ? lane + 64 * k : kLinesWg - 1);
+            tline[k] = t < kLines ? t : kLines - 1;
+        }
+        Frag ab0[NRT], ab1[2];
+        us8 vr[2];
+        f32x4 gr;
+        auto load_prep = [&](int n) {
+            const us8* src = reinterpret_cast<const us8*>(vrow(n));
+            vr[0] = src[0];
+            vr[1] = src[1];
+            const E* hb = hptr(n);
+#pragma unroll
+            for (int r = 0; r < NRT; ++r) {
+                ab0[r] = load_frag<Frag, E>(hb + HO::kAb, r * 2, lane);
+                if (r >= 2) ab1[r - 2] = load_frag<Frag, E>(hb + HO::kAb, r * 2 + 1, lane);
+            }
+            gr = *reinterpret_cast<const f32x4*>(
+                reinterpret_cast<const float*>(reinterpret_cast<const unsigned char*>(hb) + HO::kGlastBytes) +
+                4 * glane);
+        };
+        // one 4-byte read in each of this column block's share of the lines of
+        // chunk n's handoff block, and in this lane's V row: brings them to L2
+        typedef float Touch[NTH + 1];
+        auto touch = [&](int n, Touch& t) {
+            const float* hb = reinterpret_cast<const float*>(hptr(n));
+#pragma unroll
+            for (int k = 0; k < NTH; ++k) t[k] = hb[tline[k] * 32];
+            t[NTH] = *reinterpret_cast<const float*>(vrow(n));
+        };
+        auto prep = [&](int n, int b) {  // into LDS buffer b
+            const bool valid = lane < chunk_len(n);
+#pragma unroll
+            for (int c = 0; c < 16; ++c) {
+                const float x = bf16_to_f32(vr[c >> 3][c & 7]);
+                sV[vslab][c + 16 * vq][ve] = (E)(valid ? x : 0.f);
+            }
+            const Frag vf0 = *reinterpret_cast<const Frag*>(&sV[0][lane][0]);
+            const Frag vf1 = *reinterpret_cast<const Frag*>(&sV[1][lane][0]);
+#pragma unroll
+            for (int r = 0; r < NRT; ++r) {
+                f32x4 u = M::run(ab0[r], vf0, f32x4{0.f, 0.f, 0.f, 0.f});
+                if (r >= 2) u = M::run(ab1[r - 2], vf1, u);
+                sU0[b][r][lane] = u;
+            }
+            if (lane < DK / 4) *reinterpret_cast<f32x4*>(&sG[b][4 * lane]) = gr;
+        };
+        float acc = 0.f;
+        Touch ta = {}, tb = {};
+        auto consume = [&](const Touch& t) {
+#pragma unroll
+            for (int k = 0; k <= NTH; ++k) acc += t[k];
+        };
+        // one chunk step: prepare chunk n + 2 (loaded one step ago), load chunk
+        // n + 3, consume the touches of two steps ago and touch chunk n + 5
+        auto iter = [&](int n, Touch& t) {
+            prep(clampc(n + 2), (n + 2) % 3);
+            __builtin_amdgcn_sched_barrier(0);
+            load_prep(clampc(n + 3));
+            __builtin_amdgcn_sched_barrier(0);
+            consume(t);
+            touch(clampc(n + 5), t);
+            __builtin_amdgcn_sched_barrier(0);
+            __syncthreads();
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        if (nch > 0) {
+            load_prep(0);
+            prep(0, 0);
+            load_prep(clampc(1));
+            prep(clampc(1), 1);
+            load_prep(clampc(2));
+            touch(clampc(3), ta);
+            touch(clampc(4), tb);
+        }
+        __syncthreads();  // U0 and Gamma of chunks 0 and 1 ready
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): as in wave 0
+        int n = 0;
+        for (; n + 1 < nch; n += 2) {
+            iter(n, ta);
+            iter(n + 1, tb);
+        }
+        if (n < nch) iter(n, ta);
+        // keeps the touches alive; no real sum has this bit pattern (a NaN payload)
+        consume(ta);
+        consume(tb);
+        if (__float_as_uint(acc) == 0x7fc0deadu) sink[lane] = acc;
+    } else {
+        // ------------------------------------------------------ outputs ----
+        // a sink slot per lane and row tile: distinct addresses, so the compiler
+        // keeps all four stores of a step (the memory waits count them)
+        float* sink_base = sink + (size_t)(id & (kSinkSlots - 1)) * kThreads * kSinkFloats;
+        Frag qd[NRT][NKS], pp0[NRT], pp1[2];
+        auto load_o = [&](int n) {  // in the order the products consume them
+            const E* hb = hptr(n);
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+                for (int r = 0; r < NRT; ++r) qd[r][ks] = load_frag<Frag, E>(hb + HO::kQd, r * NKS + ks, lane);
+#pragma unroll
+            for (int r = 0; r < NRT; ++r) pp0[r] = load_frag<Frag, E>(hb + HO::kP, r * 2, lane);
+            pp1[0] = load_frag<Frag, E>(hb + HO::kP, 5, lane);
+            pp1[1] = load_frag<Frag, E>(hb + HO::kP, 7, lane);
+        };
+        // O(n)^T from the fragments wave 0 left at parity n & 1; lane (q, m)
+        // holds token 16 r + m, columns 4q .. 4q+3. n = -1 is a dry run whose
+        // stores all go to the sink (it keeps the loop free of branches).
+        auto output = [&](int n, int pn) {
+            const int par = n & 1;
+            Frag sf[NKS], uf[2];
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) sf[ks] = *reinterpret_cast<const Frag*>(&sSU[par][ks][lane][0]);
+            uf[0] = *reinterpret_cast<const Frag*>(&sSU[par][NKS][lane][0]);
+            uf[1] = *reinterpret_cast<const Frag*>(&sSU[par][NKS + 1][lane][0]);
+            f32x4 O[NRT];
+#pragma unroll
+            for (int r = 0; r < NRT; ++r) O[r] = M::run(sf[0], qd[r][0], f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+            for (int ks = 1; ks < NKS; ++ks)
+#pragma unroll
+                for (int r = 0; r < NRT; ++r) O[r] = M::run(sf[ks], qd[r][ks], O[r]);
+#pragma unroll
+            for (int r = 0; r < NRT; ++r) {
+                O[r] = M::run(uf[0], pp0[r], O[r]);
+                if (r >= 2) O[r] = M::run(uf[1], pp1[r - 2], O[r]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            load_o(pn);
+            __builtin_amdgcn_sched_barrier(0);
+            const int len = n < 0 ? 0 : chunk_len(n);
+            const int64_t tok0 = tstart + (int64_t)n * C;
+#pragma unroll
+            for (int r = 0; r < NRT; ++r) {
+                const int tok = 16 * r + m;
+                float* op = tok < len ? o + ((tok0 + tok) * H + h) * (int64_t)DV + j0 + 4 * q
+                                      : sink_base + (size_t)(64 * r + lane) * kSinkFloats;
+                *reinterpret_cast<f32x4*>(op) = O[r];
+            }
+        };
+        if (nch > 0) load_o(0);
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): as in wave 0
+        for (int n = 0; n < nch; ++n) {
+            output(n - 1, n);
+            __syncthreads();
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (nch > 0) output(nch - 1, nch - 1);
+    }
+}
+
+// Five-wave scan: one workgroup = one (sequence, head) and two column blocks
+// of 16 value columns, on one CU. A CU's vector-memory path delivers about
+// 50 B/clk from L2, and that bounds a scan step; so the operands both column
+// blocks need (W, Kc^T; Qd, P) are fetched once per CU.
+//   waves 0, 1  the chains of the two column blocks: U = U0 - W S, then
+//               S <- diag(Gamma_last) S + Kc^T U, with S in registers and W,
+//               Kc^T read from LDS one step ahead.
+//   wave 2      outputs of both blocks, one chunk behind the chains:
+//               O^T = S^T Qd^T + U^T P^T (Qd and P loaded once for both).
+//   wave 3      preparation, two chunks ahead: V tiles, U0 = Ab V for both
+//               blocks and Gamma_last into LDS.
+//   wave 4      loader: W and Kc^T straight into a three-slot LDS ring three
+//               chunks ahead, and touches of the lines five chunks ahead.
+// One barrier per chunk. Vector memory counters complete in issue order, so
+// every wave drains its prologue loads before its loop and issues each
+// loop's loads in a fixed order; the V and handoff pointers are not
+// __restrict__, which keeps prefetches from moving across the barriers.
+template <int DK, int DV>
+__global__ __launch_bounds__(320) __attribute__((amdgpu_waves_per_eu(1, 2))) void k2_quad_kernel(
+    const void* vin, const int32_t* __restrict__ cu, const int32_t* __restrict__ order,
+    const int32_t* __restrict__ chunk_start, const int32_t* __restrict__ ckpt_base, int npairs,
+    int64_t N, int H, int64_t max_chunks, const unsigned char* handoff,
+    const float* __restrict__ s0, float* __restrict__ sfinal, int64_t interval,
+    float* __restrict__ ckpt, int64_t ckpt_rows, float* __restrict__ o, float* __restrict__ sink) {
+    using M = Mma<true>;
+    using E = _Float16;
+    using Frag = half8;
+    using HO = Handoff<DK, true>;
+    typedef unsigned short us8 __attribute__((ext_vector_type(8)));
+    constexpr int NKS = DK / 32;    // K slabs over channels
+    constexpr int NST = DK / 16;    // state row tiles
+    constexpr int NRT = C / 16;     // token row tiles
+    constexpr int NVB = DV / 16;    // column blocks per (seq, head)
+    constexpr int NWG = NVB / 2;    // workgroups per (seq, head)
+    constexpr int NWF = NRT * NKS;  // W fragments per chunk
+    constexpr int NKF = NST * 2;    // Kc^T fragments per chunk
+    constexpr int kLines = (int)(HO::kBytes / 128);     // 128-byte lines per handoff block
+    constexpr int kLinesWg = (kLines + NWG - 1) / NWG;  // lines each workgroup touches
+    constexpr int NTH = (kLinesWg + 63) / 64;           // handoff touches per lane
+
+    __shared__ __attribute__((aligned(16))) E sWK[3][NWF + NKF][64][8];   // W then Kc^T fragments
+    __shared__ __attribute__((aligned(16))) f32x4 sU0[3][2][NRT][64];      // U0 per block (result layout)
+    __shared__ __attribute__((aligned(16))) float sG[3][DK];               // Gamma_last
+    __shared__ __attribute__((aligned(16))) E sSU[2][2][NKS + 2][64][8];   // [parity][block] S, U fragments
+    __shared__ __attribute__((aligned(16))) E sV[2][2][64][8];             // prep: V tiles [block][slab] (swizzled rows)
+    __shared__ __attribute__((aligned(16))) float sTrash[64];              // loader: target of the L2 touches
+
+    const int id = blockIdx.x;
+    const int xcd = id & 7, slot = id >> 3;
+    const int pair = xcd + 8 * (slot / NWG);
+    const int j0 = (slot % NWG) * 32;  // first of the workgroup's 32 columns
+    if (pair >= npairs) return;
+    const int rank = pair / H, h = pair % H;
+    const int seq = order ? order[rank] : rank;
+    int64_t tstart = 0, L = N;
+    if (cu) seq_range(cu, seq, N, tstart, L);
+    const int cbase = chunk_start ? chunk_start[seq] : 0;
+    int nch = (int)((L + C - 1) / C);
+    if (cbase + (int64_t)nch > max_chunks) nch = cbase < max_chunks ? (int)(max_chunks - cbase) : 0;
+    const int last = nch > 0 ? nch - 1 : 0;
+    auto clampc = [&](int n) { return n < last ? n : last; };
+
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int q = lane >> 4;
+    const int m = lane & 15;
+    const unsigned char* hbase = handoff + ((size_t)h * max_chunks + cbase) * HO::kBytes;
+    auto hptr = [&](int n) { return reinterpret_cast<const E*>(hbase + (size_t)n * HO::kBytes); };
+    auto chunk_len = [&](int n) {
+        const int64_t left = L - (int64_t)n * C;
+        return left < C ? (int)left : C;
+    };
+    const unsigned short* V = static_cast<const unsigned short*>(vin);
+    // this lane's V row of chunk n (rows past the end repeat the last valid row)
+    auto vrow = [&](int n) {
+        const int64_t left = L - (int64_t)n * C;
+        const int64_t tok = tstart + (int64_t)n * C + (lane < left ? lane : left - 1);
+        return V + (tok * H + h) * (int64_t)DV + j0;
+    };
+
+    if (wave < 2) {
+        // ----------------------------------------------------- the chains ----
+        const int cb = wave, jc = j0 + 16 * cb;
+        Frag wn[NRT][NKS], kc[NST][2];
+        f32x4 u0[NRT], gl[NST];
+        auto read_w = [&](int n) {
+            const E* b = &sWK[n % 3][0][0][0];
+#pragma unroll
+            for (int r = 0; r < NRT; ++r)
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks)
+                    wn[r][ks] = *reinterpret_cast<const Frag*>(b + ((r * NKS + ks) * 64 + lane) * 8);
+        };
+        auto read_k = [&](int n) {
+            const E* b = &sWK[n % 3][NWF][0][0];
+#pragma unroll
+            for (int i = 0; i < NST; ++i) {
+                kc[i][0] = *reinterpret_cast<const Frag*>(b + ((i * 2 + 0) * 64 + lane) * 8);
+                kc[i][1] = *reinterpret_cast<const Frag*>(b + ((i * 2 + 1) * 64 + lane) * 8);
+            }
+        };
+        auto read_prep = [&](int n) {
+            const int b = n % 3;
+#pragma unroll
+            for (int r = 0; r < NRT; ++r) u0[r] = sU0[b][cb][r][lane];
+#pragma unroll
+            for (int i = 0; i < NST; ++i) gl[i] = *reinterpret_cast<const f32x4*>(&sG[b][16 * i + 4 * q]);
+        };
+        // state rows owned: channel 16 i + 4 q + ii, column jc + m
+        f32x4 S[NST];
+        const size_t sbase = ((size_t)seq * H + h) * DK * DV;
+        if (s0) {
+#pragma unroll
+            for (int i = 0; i < NST; ++i)
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) S[i][ii] = s0[sbase + (size_t)(16 * i + 4 * q + ii) * DV + jc + m];
+        } else {
+#pragma unroll
+            for (int i = 0; i < NST; ++i) S[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        auto store_state = [&](float* dst) {
+#pragma unroll
+            for (int i = 0; i < NST; ++i)
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) dst[(size_t)(16 * i + 4 * q + ii) * DV + jc + m] = S[i][ii];
+        };
+        auto step = [&](int n) {
+            const int par = n & 1;
+            // U = U0 - W S, slab by slab as S converts; S <- Gamma S meanwhile
+            Frag sf[NKS];
+            f32x4 U[NRT];
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) {
+                    sf[ks][ii] = (E)S[2 * ks][ii];
+                    sf[ks][4 + ii] = (E)S[2 * ks + 1][ii];
+                }
+#pragma unroll
+                for (int r = 0; r < NRT; ++r) U[r] = M::run(wn[r][ks], sf[ks], ks == 0 ? u0[r] : U[r]);
+            }
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) *reinterpret_cast<Frag*>(&sSU[par][cb][ks][lane][0]) = sf[ks];
+#pragma unroll
+            for (int i = 0; i < NST; ++i) S[i] = S[i] * gl[i];
+            __builtin_amdgcn_sched_barrier(0);
+            read_w(n + 1);
+            read_prep(n + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            Frag uf[2];
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) {
+                    uf[s][ii] = (E)U[2 * s][ii];
+                    uf[s][4 + ii] = (E)U[2 * s + 1][ii];
+                }
+                *reinterpret_cast<Frag*>(&sSU[par][cb][NKS + s][lane][0]) = uf[s];
+            }
+            // S <- diag(Gamma_last) S + Kc^T U
+#pragma unroll
+            for (int i = 0; i < NST; ++i) {
+                const f32x4 a = M::run(kc[i][0], uf[0], S[i]);
+                S[i] = M::run(kc[i][1], uf[1], a);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            read_k(n + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            __syncthreads();
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        __syncthreads();  // chunks 0 and 1 staged
+        __builtin_amdgcn_sched_barrier(0);
+        read_w(0);
+        read_k(0);
+        read_prep(0);
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the loop waits only on its own loads
+        // Chunks run in segments that end on checkpoint boundaries, so the
+        // chunk loop itself never branches; each checkpoint is stored between
+        // segments. Without checkpoints there is one segment.
+        const int ick = interval > 0 ? (int)(interval / C) : (nch > 0 ? nch : 1);
+        int64_t cidx = ckpt_base ? ckpt_base[seq] : 0;
+        for (int seg0 = 0; seg0 < nch; seg0 += ick) {
+            const int seg1 = seg0 + ick < nch ? seg0 + ick : nch;
+            for (int n = seg0; n < seg1; ++n) step(n);
+            if (interval > 0 && (int64_t)seg1 * C <= L && seg1 - seg0 == ick) {
+                if (cidx < ckpt_rows) store_state(ckpt + (cidx * H + h) * (size_t)DK * DV);
+                ++cidx;
+                __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): drain the (rare) checkpoint stores
+            }
+        }
+        if (sfinal) store_state(sfinal + sbase);
+    } else if (wave == 4) {
+        // ------------------------------------------------------- loader ----
+        // W and Kc^T go global -> LDS directly (no registers), three chunks
+        // ahead into the ring slot the chains finished with one step ago.
+        // Before each barrier the loader waits only for the chunk the chains
+        // read next (issued one step earlier), so later loads stay in flight.
+        // It touches no LDS itself: the compiler would drain every load in
+        // flight before such an access.
+        typedef __attribute__((address_space(3))) void* lds_ptr;
+        int tline[NTH];
+#pragma unroll
+        for (int k = 0; k < NTH; ++k) {
+            const int t = (slot % NWG) * kLinesWg + (lane + 64 * k < kLinesWg ? lane + 64 * k : kLinesWg - 1);
+            tline[k] = t < kLines ? t : kLines - 1;
+        }
+        auto dma_wk = [&](int n) {
+            const E* hb = hptr(n);
+            const int bf = n % 3;
+#pragma unroll
+            for (int f = 0; f < NWF; ++f)
+                __builtin_amdgcn_global_load_lds((const void*)(hb + HO::kW + ((size_t)f * 64 + lane) * 8),
+                                                 (lds_ptr)&sWK[bf][f][0][0], 16, 0, 0);
+#pragma unroll
+            for (int f = 0; f < NKF; ++f)
+                __builtin_amdgcn_global_load_lds((const void*)(hb + HO::kKc + ((size_t)f * 64 + lane) * 8),
+                                                 (lds_ptr)&sWK[bf][NWF + f][0][0], 16, 0, 0);
+        };
+        // one 4-byte read in each of this workgroup's share of the lines of
+        // chunk n's handoff block and in this lane's V row: brings them to L2.
+        // The touches load into an LDS area nobody reads, so no register has
+        // to wait for them.
+        auto touch = [&](int n) {
+            const float* hb = reinterpret_cast<const float*>(hptr(n));
+#pragma unroll
+            for (int k = 0; k < NTH; ++k)
+                __builtin_amdgcn_global_load_lds((const void*)(hb + tline[k] * 32), (lds_ptr)&sTrash[0], 4, 0, 0);
+            __builtin_amdgcn_global_load_lds((const void*)vrow(n), (lds_ptr)&sTrash[0], 4, 0, 0);
+        };
+        // Per step, in this order: the DMA (NWF + NKF) and the touches
+        // (NTH + 1). The DMA of chunk n + 2 (issued one step ago) has completed
+        // once at most kAfter later operations remain outstanding.
+        constexpr int kAfter = (NTH + 1) + (NWF + NKF) + (NTH + 1);
+        static_assert(kAfter <= 63, "the memory counter field holds at most 63");
+        auto bar = [&]() {  // barrier without the compiler's full memory drain
+            __builtin_amdgcn_s_waitcnt(0x0F70 | (kAfter & 15) | ((kAfter >> 4) << 14));  // vmcnt(kAfter)
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+        };
+        if (nch > 0) {
+            dma_wk(0);
+            dma_wk(clampc(1));
+            dma_wk(clampc(2));
+            touch(clampc(3));
+            touch(clampc(4));
+        }
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): chunks 0-2 complete
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();  // chunks 0 and 1 staged
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        for (int n = 0; n < nch; ++n) {
+            // DMA chunk n + 3, touch chunk n + 5
+            dma_wk(clampc(n + 3));
+            __builtin_amdgcn_sched_barrier(0);
+            touch(clampc(n + 5));
+            __builtin_amdgcn_sched_barrier(0);
+            bar();
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    } else if (wave == 3) {
+        // -------------------------------------------------- preparation ----
+        const int glane = lane < DK / 4 ? lane : 0;  // Gamma_last: lane holds channels 4l..4l+3
+        // V: instruction i loads rows 16 i + lane / 4, 16-byte piece lane % 4 of
+        // the workgroup's 64-byte row segment (coalesced: four lanes per row)
+        const int vpiece = lane & 3;
+        Frag ab0[NRT], ab1[2];
+        us8 vr[4];
+        f32x4 gr;
+        auto load_prep = [&](int n) {
+            const int64_t left = L - (int64_t)n * C;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * i + (lane >> 2);
+                const int64_t tok = tstart + (int64_t)n * C + (r < left ? r : left - 1);
+                vr[i] = *reinterpret_cast<const us8*>(V + (tok * H + h) * (int64_t)DV + j0 + 8 * vpiece);
+            }
+            const E* hb = hptr(n);
+#pragma unroll
+            for (int r = 0; r < NRT; ++r) {
+                ab0[r] = load_frag<Frag, E>(hb + HO::kAb, r * 2, lane);
+                if (r >= 2) ab1[r - 2] = load_frag<Frag, E>(hb + HO::kAb, r * 2 + 1, lane);
+            }
+            gr = *reinterpret_cast<const f32x4*>(
+                reinterpret_cast<const float*>(reinterpret_cast<const unsigned char*>(hb) + HO::kGlastBytes) +
+                4 * glane);
+        };
+        // V tile rows are stored XOR-swizzled (row R of block b at R ^ (R / 16 | 4 b)),
+        // which keeps both the scattered 2-byte writes and the fragment reads
+        // free of bank conflicts.
+        auto prep = [&](int n) {  // V tiles, U0 = Ab V of both blocks and Gamma_last into buffer n mod 3
+            const int bf = n % 3;
+            const int len = chunk_len(n);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * i + (lane >> 2);  // token
+                const int slab = r >> 5, w32 = r & 31;
+                const int vq = (w32 & 15) >> 2, ve = (w32 & 3) + ((w32 >> 4) << 2);
+                const int bk = vpiece >> 1;
+                const bool valid = r < len;
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const int c = 8 * (vpiece & 1) + k;
+                    const int R = c + 16 * vq;
+                    const float x = bf16_to_f32(vr[i][k]);
+                    sV[bk][slab][R ^ (vq | (bk << 2))][ve] = (E)(valid ? x : 0.f);
+                }
+            }
+            const int rsw = lane ^ (lane >> 4);
+#pragma unroll
+            for (int bk = 0; bk < 2; ++bk) {
+                const Frag vf0 = *reinterpret_cast<const Frag*>(&sV[bk][0][rsw ^ (bk << 2)][0]);
+                const Frag vf1 = *reinterpret_cast<const Frag*>(&sV[bk][1][rsw ^ (bk << 2)][0]);
+#pragma unroll
+                for (int r = 0; r < NRT; ++r) {
+                    f32x4 u = M::run(ab0[r], vf0, f32x4{0.f, 0.f, 0.f, 0.f});
+                    if (r >= 2) u = M::run(ab1[r - 2], vf1, u);
+                    sU0[bf][bk][r][lane] = u;
+                }
+            }
+            if (lane < DK / 4) *reinterpret_cast<f32x4*>(&sG[bf][4 * lane]) = gr;
+        };
+        if (nch > 0) {
+            load_prep(0);
+            prep(0);
+            load_prep(clampc(1));
+            prep(clampc(1));
+            load_prep(clampc(2));
+        }
+        __syncthreads();  // chunks 0 and 1 staged
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): as in the chains
+        for (int n = 0; n < nch; ++n) {
+            // stage chunk n + 2 (loaded one step ago), load chunk n + 3
+            prep(clampc(n + 2));
+            __builtin_amdgcn_sched_barrier(0);
+            load_prep(clampc(n + 3));
+            __builtin_amdgcn_sched_barrier(0);
+            __syncthreads();
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    } else {
+        // ------------------------------------------------------ outputs ----
+        // a sink slot per lane, row tile and block: distinct addresses, so the
+        // compiler keeps every store of a step (the memory waits count them)
+        float* sink_base = sink + (size_t)(id & (kSinkSlots - 1)) * kThreads * kSinkFloats;
+        Frag qd[NRT][NKS], pp0[NRT], pp1[2];
+        auto load_o = [&](int n) {  // in the order the products consume them
+            const E* hb = hptr(n);
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+                for (int r = 0; r < NRT; ++r) qd[r][ks] = load_frag<Frag, E>(hb + HO::kQd, r * NKS + ks, lane);
+#pragma unroll
+            for (int r = 0; r < NRT; ++r) pp0[r] = load_frag<Frag, E>(hb + HO::kP, r * 2, lane);
+            pp1[0] = load_frag<Frag, E>(hb + HO::kP, 5, lane);
+            pp1[1] = load_frag<Frag, E>(hb + HO::kP, 7, lane);
+        };
+        // O(n)^T of both blocks from the fragments the chains left at parity
+        // n & 1; lane (q, m) holds token 16 r + m, columns 4q .. 4q+3. n = -1
+        // is a dry run whose stores all go to the sink (no branch in the loop).
+        auto output = [&](int n, int pn) {
+            const int par = n & 1;
+            f32x4 O[2][NRT];
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                Frag sf[NKS], uf[2];
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) sf[ks] = *reinterpret_cast<const Frag*>(&sSU[par][b][ks][lane][0]);
+                uf[0] = *reinterpret_cast<const Frag*>(&sSU[par][b][NKS][lane][0]);
+                uf[1] = *reinterpret_cast<const Frag*>(&sSU[par][b][NKS + 1][lane][0]);
+#pragma unroll
+                for (int r = 0; r < NRT; ++r) O[b][r] = M::run(sf[0], qd[r][0], f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                for (int ks = 1; ks < NKS; ++ks)
+#pragma unroll
+                    for (int r = 0; r < NRT; ++r) O[b][r] = M::run(sf[ks], qd[r][ks], O[b][r]);
+#pragma unroll
+                for (int r = 0; r < NRT; ++r) {
+                    O[b][r] = M::run(uf[0], pp0[r], O[b][r]);
+                    if (r >= 2) O[b][r] = M::run(uf[1], pp1[r - 2], O[b][r]);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            load_o(pn);
+            __builtin_amdgcn_sched_barrier(0);
+            const int len = n < 0 ? 0 : chunk_len(n);
+            const int64_t tok0 = tstart + (int64_t)n * C;
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int r = 0; r < NRT; ++r) {
+                    const int tok = 16 * r + m;
+                    float* op = tok < len ? o + ((tok0 + tok) * H + h) * (int64_t)DV + j0 + 16 * b + 4 * q
+                                          : sink_base + (size_t)(64 * r + lane) * kSinkFloats + 4 * b;
+                    *reinterpret_cast<f32x4*>(op) = O[b][r];
+                }
+        };
+        if (nch > 0) load_o(0);
+        __syncthreads();  // chunks 0 and 1 staged
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): as in the chains
+        for (int n = 0; n < nch; ++n) {
+            output(n - 1, n);
+            __syncthreads();
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (nch > 0) output(nch - 1, nch - 1);
+    }
+}
+
 // ------------------------------------------------------------- host side ---
 struct Plan {
     int32_t* chunk_start;
@@ -986,6 +1772,48 @@ void launch_scan(const PrefillArgs& a, const Plan& p, int npairs, hipStream_t st
                        a.ckpt_interval, a.ckpt_states, a.ckpt_rows, a.o, p.sink);
 }
 
+// Three-wave scan: one workgroup per (pair, 16 columns). When there are fewer
+// such workgroups than 4 per CU, each asks for enough (unused) LDS that at
+// most ceil(workgroups / CUs) of them share a CU, so they spread out instead
+// of queueing on one CU's vector memory path.
+template <int DK, int DV, int NCB>
+void launch_trio(const PrefillArgs& a, const Plan& p, int npairs, int cus, int lds_max,
+                 hipStream_t stream) {
+    constexpr int NWG = DV / 16 / NCB;  // workgroups per (seq, head)
+    const bool varlen = a.cu_seqlens != nullptr;
+    const int64_t groups = (npairs + 7) / 8;
+    const unsigned grid = (unsigned)(groups * 8 * NWG);
+    const int64_t wgs = (int64_t)npairs * NWG;
+    const int64_t per_cu = (wgs + cus - 1) / cus;
+    unsigned pad = 0;
+    hipFuncAttributes fa;
+    if (per_cu < 2 && hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(&k2_trio_kernel<DK, DV, NCB>)) == hipSuccess) {
+        const int64_t want = (int64_t)lds_max / per_cu - 512;
+        const int64_t have = (int64_t)fa.sharedSizeBytes;
+        pad = want > have ? (unsigned)(want - have) : 0u;
+    }
+    hipLaunchKernelGGL((k2_trio_kernel<DK, DV, NCB>), dim3(grid), dim3(192 * NCB), pad, stream,
+                       a.v, a.cu_seqlens, varlen ? p.order : nullptr,
+                       varlen ? p.chunk_start : nullptr, varlen ? p.ckpt_base : nullptr, npairs,
+                       a.total_tokens, a.H, p.max_chunks, p.handoff, a.initial_state, a.final_state,
+                       a.ckpt_interval, a.ckpt_states, a.ckpt_rows, a.o, p.sink);
+}
+
+// Five-wave scan: one workgroup per (pair, 32 columns), one per CU (its LDS
+// use, about 150 KB, keeps a second one off the CU).
+template <int DK, int DV>
+void launch_quad(const PrefillArgs& a, const Plan& p, int npairs, hipStream_t stream) {
+    constexpr int NWG = DV / 32;
+    const bool varlen = a.cu_seqlens != nullptr;
+    const int64_t groups = (npairs + 7) / 8;
+    const unsigned grid = (unsigned)(groups * 8 * NWG);
+    hipLaunchKernelGGL((k2_quad_kernel<DK, DV>), dim3(grid), dim3(320), 0, stream,
+                       a.v, a.cu_seqlens, varlen ? p.order : nullptr,
+                       varlen ? p.chunk_start : nullptr, varlen ? p.ckpt_base : nullptr, npairs,
+                       a.total_tokens, a.H, p.max_chunks, p.handoff, a.initial_state, a.final_state,
+                       a.ckpt_interval, a.ckpt_states, a.ckpt_rows, a.o, p.sink);
+}
+
 template <int DK, int DV, bool BF16>
 hipError_t launch_typed(const PrefillArgs& a, hipStream_t stream) {
     const Plan p = make_plan(a);
@@ -995,45 +1823,48 @@ hipError_t launch_typed(const PrefillArgs& a, hipStream_t stream) {
         hipLaunchKernelGGL(prep_kernel, dim3(1), dim3(kThreads), 0, stream, a.cu_seqlens, a.num_seqs,
                            a.total_tokens, a.ckpt_interval, p.chunk_start, p.ckpt_base, p.order);
     if (prepare && p.max_chunks > 0 && a.total_tokens > 0)
-        hipLaunchKernelGGL((k1_prep_kernel<DK, BF16>), dim3((unsigned)p.max_chunks, (unsigned)a.H),
+        hipLaunchKernelGGL((k1_prep_kernel<DK, BF16>), dim3((unsigned)(p.max_chunks * a.H)),
                            dim3(kThreads), 0, stream, a.q, a.k, a.g, a.beta, a.cu_seqlens,
                            varlen ? p.chunk_start : nullptr, a.num_seqs, a.total_tokens, a.H,
                            p.max_chunks, p.handoff);
-    // Value columns per scan workgroup. Every workgroup streams the whole
-    // handoff of its (sequence, head) through its CU, so wider column blocks
-    // cost fewer bytes per column but more serial work per chunk. Measured
-    // chunk-step times on MI355X for 16, 32 and 64 columns: about 1.73, 2.11
-    // and 3.08 us. Pick the width with the least (rounds of workgroups over the
-    // CUs) x (step time); fp32 operands are twice as wide, so that path keeps 16.
+    // Scan design. Every scan workgroup streams the whole handoff of its
+    // (sequence, head) through its CU, about 63 KB per chunk for D = 128, and
+    // a CU's vector-memory path (~50 B/clk from L2) bounds each chunk step.
+    // Measured chunk-step times on MI355X (D = 128): three-wave kernel, one
+    // 16-column block per CU: 1.35 us; five-wave kernel, two blocks sharing a
+    // CU's operand stream: 1.58 us; four-wave kernel with 64 columns: 3.08 us
+    // (with 16 or 32 columns, 1.73 and 2.11 us: never the best choice). Pick
+    // the least (rounds of workgroups over the CUs) x (step time): few
+    // (sequence, head) pairs take the three-wave kernel, a few times more the
+    // five-wave one, thousands the 64-column one. fp32 operands take the
+    // four-wave kernel with 16 columns.
     const int npairs = a.num_seqs * a.H;
-    int cus = 256;
+    int cus = 256, lds_max = 65536;
     {
         int dev = 0;
         if (hipGetDevice(&dev) == hipSuccess) {
             int n = 0;
             if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
                 cus = n;
+            if (hipDeviceGetAttribute(&n, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) == hipSuccess && n > 0)
+                lds_max = n;
         }
     }
-    int nt = 1;
+    enum { kTrio, kQuad, kNt4, kNt1 } design = kNt1;
     if (BF16) {
-        const int64_t step_cost[3] = {173, 211, 308};
-        int64_t best = -1;
-        for (int li = 0; li < 3; ++li) {
-            const int cand = 1 << li;
-            if (DV % (16 * cand) != 0) continue;
-            const int64_t wgs = (int64_t)npairs * (DV / (16 * cand));
-            const int64_t cost = (wgs + cus - 1) / cus * step_cost[li];
-            if (best < 0 || cost < best) {
-                best = cost;
-                nt = cand;
-            }
-        }
+        const int64_t blocks = (int64_t)npairs * (DV / 16);  // 16-column blocks
+        auto rounds = [&](int64_t wgs) { return (wgs + cus - 1) / cus; };
+        const int64_t trio = rounds(blocks) * 135, quad = rounds(blocks / 2) * 158;
+        const int64_t nt4 = DV % 64 == 0 ? rounds(blocks / 4) * 308 : INT64_MAX;
+        design = trio <= quad && trio <= nt4 ? kTrio : (quad <= nt4 ? kQuad : kNt4);
     }
     if (scan) {
-        if (nt == 4) launch_scan<DK, DV, 4, BF16>(a, p, npairs, stream);
-        else if (nt == 2) launch_scan<DK, DV, 2, BF16>(a, p, npairs, stream);
-        else launch_scan<DK, DV, 1, BF16>(a, p, npairs, stream);
+        switch (design) {
+            case kTrio: launch_trio<DK, DV, 1>(a, p, npairs, cus, lds_max, stream); break;
+            case kQuad: launch_quad<DK, DV>(a, p, npairs, stream); break;
+            case kNt4: launch_scan<DK, DV, 4, BF16>(a, p, npairs, stream); break;
+            default: launch_scan<DK, DV, 1, BF16>(a, p, npairs, stream); break;
+        }
     }
     return hipGetLastError();
 }

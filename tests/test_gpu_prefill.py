@@ -240,3 +240,13 @@ def test_long_tail_with_checkpoints():
     x = make_prefill([64 * 37 + 19, 64 * 5], 2, 128, 128, "bf16", 46, init_state=True,
                      ckpt_interval=128)
     check_full(x, "long tail + checkpoints")
+
+
+@pytest.mark.parametrize("Dk,Dv,nseq", [(128, 128, 2), (64, 64, 3), (128, 64, 3), (64, 128, 2)])
+def test_pair_counts_between_designs(Dk, Dv, nseq):
+    """32 heads and two or three sequences: on a 256-CU device these counts of
+    (sequence, head) pairs select the scan whose two column blocks share one
+    CU's operand stream; checked in full against the oracle."""
+    lengths = [700, 333, 517][:nseq]
+    x = make_prefill(lengths, 32, Dk, Dv, "bf16", 47, init_state=True, ckpt_interval=128)
+    check_full(x, f"{nseq} seqs x 32 heads")
