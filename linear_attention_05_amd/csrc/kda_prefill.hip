@@ -1039,12 +1039,6 @@ __global__ __launch_bounds__(192 * NCB) __attribute__((amdgpu_waves_per_eu(1, 2)
         return left < C ? (int)left : C;
     };
     const unsigned short* V = static_cast<const unsigned short*>(vin);
-    // this lane's V row of chunk n (rows past the end repeat the last valid row)
-    auto vrow = [&](int n) {
-        const int64_t left = L - (int64_t)n * C;
-        const int64_t tok = tstart + (int64_t)n * C + (lane < left ? lane : left - 1);
-        return V + (tok * H + h) * (int64_t)DV + j0;
-    };
 
     if (role == 0) {
         // ------------------------------------------------------ the chain ----
@@ -1164,9 +1158,9 @@ __global__ __launch_bounds__(192 * NCB) __attribute__((amdgpu_waves_per_eu(1, 2)
         if (sfinal) store_state(sfinal + sbase);
     } else if (role == 2) {
         // ------------------------------------------ next-chunk preparation ----
-        // V staging: this lane's token -> slab, B-frag lane group and slot (inverse of perm32)
-        const int vslab = lane >> 5, w32 = lane & 31;
-        const int vq = (w32 & 15) >> 2, ve = (w32 & 3) + ((w32 >> 4) << 2);
+        // V: load instruction i covers rows 32 i + lane / 2, 16-byte half
+        // lane % 2 of the row's 32-byte segment (two lanes per row)
+        const int vhalf = lane & 1;
         const int glane = lane < DK / 4 ? lane : 0;  // Gamma_last: lane holds channels 4l..4l+3
         int tline[NTH];  // this lane's lines of a handoff block (clamped into the block)
 #pragma unroll
@@ -1178,9 +1172,13 @@ __global__ __launch_bounds__(192 * NCB) __attribute__((amdgpu_waves_per_eu(1, 2)
         us8 vr[2];
         f32x4 gr;
         auto load_prep = [&](int n) {
-            const us8* src = reinterpret_cast<const us8*>(vrow(n));
-            vr[0] = src[0];
-            vr[1] = src[1];
+            const int64_t left = L - (int64_t)n * C;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int r = 32 * i + (lane >> 1);
+                const int64_t tok = tstart + (int64_t)n * C + (r < left ? r : left - 1);
+                vr[i] = *reinterpret_cast<const us8*>(V + (tok * H + h) * (int64_t)DV + j0 + 8 * vhalf);
+            }
             const E* hb = hptr(n);
 #pragma unroll
             for (int r = 0; r < NRT; ++r) {
@@ -1193,22 +1191,44 @@ __global__ __launch_bounds__(192 * NCB) __attribute__((amdgpu_waves_per_eu(1, 2)
         };
         // one 4-byte read in each of this column block's share of the lines of
         // chunk n's handoff block, and in this lane's V row: brings them to L2
+        // V: a row of the head spans DV / 64 lines, shared by all the head's
+        // column blocks; this workgroup touches every line of its own share of
+        // the chunk's rows (lane i: line i % LPV of row i / LPV of the share)
+        constexpr int LPV = DV / 64;                   // 128-byte lines per V row
+        constexpr int VROWS = (C + NVB - 1) / NVB;     // rows this workgroup touches
+        const int vt_row = vb * VROWS + (lane / LPV < VROWS ? lane / LPV : VROWS - 1);
+        const int vt_line = lane % LPV;
         typedef float Touch[NTH + 1];
         auto touch = [&](int n, Touch& t) {
             const float* hb = reinterpret_cast<const float*>(hptr(n));
 #pragma unroll
             for (int k = 0; k < NTH; ++k) t[k] = hb[tline[k] * 32];
-            t[NTH] = *reinterpret_cast<const float*>(vrow(n));
+            const int64_t left = L - (int64_t)n * C;
+            const int r = vt_row < C ? vt_row : C - 1;
+            const int64_t tok = tstart + (int64_t)n * C + (r < left ? r : left - 1);
+            t[NTH] = *reinterpret_cast<const float*>(V + (tok * H + h) * (int64_t)DV + 64 * vt_line);
         };
+        // V tile rows are stored XOR-swizzled (row R at R ^ (R / 16)), which
+        // keeps both the scattered 2-byte writes and the fragment reads free of
+        // bank conflicts.
         auto prep = [&](int n, int b) {  // into LDS buffer b
-            const bool valid = lane < chunk_len(n);
+            const int len = chunk_len(n);
 #pragma unroll
-            for (int c = 0; c < 16; ++c) {
-                const float x = bf16_to_f32(vr[c >> 3][c & 7]);
-                sV[vslab][c + 16 * vq][ve] = (E)(valid ? x : 0.f);
+            for (int i = 0; i < 2; ++i) {
+                const int r = 32 * i + (lane >> 1);  // token
+                const int w32 = r & 31;
+                const int vq = (w32 & 15) >> 2, ve = (w32 & 3) + ((w32 >> 4) << 2);
+                const bool valid = r < len;
+#pragma unroll
+                for (int kk = 0; kk < 8; ++kk) {
+                    const int R = 8 * vhalf + kk + 16 * vq;
+                    const float x = bf16_to_f32(vr[i][kk]);
+                    sV[i][R ^ vq][ve] = (E)(valid ? x : 0.f);
+                }
             }
-            const Frag vf0 = *reinterpret_cast<const Frag*>(&sV[0][lane][0]);
-            const Frag vf1 = *reinterpret_cast<const Frag*>(&sV[1][lane][0]);
+            const int rsw = lane ^ (lane >> 4);
+            const Frag vf0 = *reinterpret_cast<const Frag*>(&sV[0][rsw][0]);
+            const Frag vf1 = *reinterpret_cast<const Frag*>(&sV[1][rsw][0]);
 #pragma unroll
             for (int r = 0; r < NRT; ++r) {
                 f32x4 u = M::run(ab0[r], vf0, f32x4{0.f, 0.f, 0.f, 0.f});
@@ -1340,8 +1360,8 @@ __global__ __launch_bounds__(192 * NCB) __attribute__((amdgpu_waves_per_eu(1, 2)
 // every wave drains its prologue loads before its loop and issues each
 // loop's loads in a fixed order; the V and handoff pointers are not
 // __restrict__, which keeps prefetches from moving across the barriers.
-template <int DK, int DV>
-__global__ __launch_bounds__(320) __attribute__((amdgpu_waves_per_eu(1, 2))) void k2_quad_kernel(
+template <int DK, int DV, int NCB>
+__global__ __launch_bounds__(64 * (NCB + 3)) __attribute__((amdgpu_waves_per_eu(1, 2))) void k2_quad_kernel(
     const void* vin, const int32_t* __restrict__ cu, const int32_t* __restrict__ order,
     const int32_t* __restrict__ chunk_start, const int32_t* __restrict__ ckpt_base, int npairs,
     int64_t N, int H, int64_t max_chunks, const unsigned char* handoff,
@@ -1356,7 +1376,10 @@ __global__ __launch_bounds__(320) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
     constexpr int NST = DK / 16;    // state row tiles
     constexpr int NRT = C / 16;     // token row tiles
     constexpr int NVB = DV / 16;    // column blocks per (seq, head)
-    constexpr int NWG = NVB / 2;    // workgroups per (seq, head)
+    constexpr int NWG = NVB / NCB;  // workgroups per (seq, head)
+    constexpr int LPR = 2 * NCB;    // prep: lanes per V row segment (16 bytes each)
+    constexpr int RPI = 64 / LPR;   // prep: V rows per load instruction
+    static_assert(NVB % NCB == 0 && (NCB == 1 || NCB == 2), "one or two column blocks per workgroup");
     constexpr int NWF = NRT * NKS;  // W fragments per chunk
     constexpr int NKF = NST * 2;    // Kc^T fragments per chunk
     constexpr int kLines = (int)(HO::kBytes / 128);     // 128-byte lines per handoff block
@@ -1364,16 +1387,16 @@ __global__ __launch_bounds__(320) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
     constexpr int NTH = (kLinesWg + 63) / 64;           // handoff touches per lane
 
     __shared__ __attribute__((aligned(16))) E sWK[3][NWF + NKF][64][8];   // W then Kc^T fragments
-    __shared__ __attribute__((aligned(16))) f32x4 sU0[3][2][NRT][64];      // U0 per block (result layout)
-    __shared__ __attribute__((aligned(16))) float sG[3][DK];               // Gamma_last
-    __shared__ __attribute__((aligned(16))) E sSU[2][2][NKS + 2][64][8];   // [parity][block] S, U fragments
-    __shared__ __attribute__((aligned(16))) E sV[2][2][64][8];             // prep: V tiles [block][slab] (swizzled rows)
+    __shared__ __attribute__((aligned(16))) f32x4 sU0[3][NCB][NRT][64];      // U0 per block (result layout)
+    __shared__ __attribute__((aligned(16))) float sG[3][DK];                 // Gamma_last
+    __shared__ __attribute__((aligned(16))) E sSU[2][NCB][NKS + 2][64][8];   // [parity][block] S, U fragments
+    __shared__ __attribute__((aligned(16))) E sV[NCB][2][64][8];             // prep: V tiles [block][slab] (swizzled rows)
     __shared__ __attribute__((aligned(16))) float sTrash[64];              // loader: target of the L2 touches
 
     const int id = blockIdx.x;
     const int xcd = id & 7, slot = id >> 3;
     const int pair = xcd + 8 * (slot / NWG);
-    const int j0 = (slot % NWG) * 32;  // first of the workgroup's 32 columns
+    const int j0 = (slot % NWG) * 16 * NCB;  // first of the workgroup's columns
     if (pair >= npairs) return;
     const int rank = pair / H, h = pair % H;
     const int seq = order ? order[rank] : rank;
@@ -1403,7 +1426,7 @@ __global__ __launch_bounds__(320) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
         return V + (tok * H + h) * (int64_t)DV + j0;
     };
 
-    if (wave < 2) {
+    if (wave < NCB) {
         // ----------------------------------------------------- the chains ----
         const int cb = wave, jc = j0 + 16 * cb;
         Frag wn[NRT][NKS], kc[NST][2];
@@ -1515,7 +1538,7 @@ __global__ __launch_bounds__(320) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
             }
         }
         if (sfinal) store_state(sfinal + sbase);
-    } else if (wave == 4) {
+    } else if (wave == NCB + 2) {
         // ------------------------------------------------------- loader ----
         // W and Kc^T go global -> LDS directly (no registers), three chunks
         // ahead into the ring slot the chains finished with one step ago.
@@ -1586,20 +1609,20 @@ __global__ __launch_bounds__(320) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
             __builtin_amdgcn_sched_barrier(0);
         }
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-    } else if (wave == 3) {
+    } else if (wave == NCB + 1) {
         // -------------------------------------------------- preparation ----
         const int glane = lane < DK / 4 ? lane : 0;  // Gamma_last: lane holds channels 4l..4l+3
-        // V: instruction i loads rows 16 i + lane / 4, 16-byte piece lane % 4 of
-        // the workgroup's 64-byte row segment (coalesced: four lanes per row)
-        const int vpiece = lane & 3;
+        // V: instruction i loads rows RPI i + lane / LPR, 16-byte piece
+        // lane % LPR of the workgroup's row segment (coalesced)
+        const int vpiece = lane % LPR;
         Frag ab0[NRT], ab1[2];
-        us8 vr[4];
+        us8 vr[LPR];
         f32x4 gr;
         auto load_prep = [&](int n) {
             const int64_t left = L - (int64_t)n * C;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 16 * i + (lane >> 2);
+            for (int i = 0; i < LPR; ++i) {
+                const int r = RPI * i + lane / LPR;
                 const int64_t tok = tstart + (int64_t)n * C + (r < left ? r : left - 1);
                 vr[i] = *reinterpret_cast<const us8*>(V + (tok * H + h) * (int64_t)DV + j0 + 8 * vpiece);
             }
@@ -1620,8 +1643,8 @@ __global__ __launch_bounds__(320) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
             const int bf = n % 3;
             const int len = chunk_len(n);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 16 * i + (lane >> 2);  // token
+            for (int i = 0; i < LPR; ++i) {
+                const int r = RPI * i + lane / LPR;  // token
                 const int slab = r >> 5, w32 = r & 31;
                 const int vq = (w32 & 15) >> 2, ve = (w32 & 3) + ((w32 >> 4) << 2);
                 const int bk = vpiece >> 1;
@@ -1636,7 +1659,7 @@ __global__ __launch_bounds__(320) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
             }
             const int rsw = lane ^ (lane >> 4);
 #pragma unroll
-            for (int bk = 0; bk < 2; ++bk) {
+            for (int bk = 0; bk < NCB; ++bk) {
                 const Frag vf0 = *reinterpret_cast<const Frag*>(&sV[bk][0][rsw ^ (bk << 2)][0]);
                 const Frag vf1 = *reinterpret_cast<const Frag*>(&sV[bk][1][rsw ^ (bk << 2)][0]);
 #pragma unroll
@@ -1689,9 +1712,9 @@ __global__ __launch_bounds__(320) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
         // is a dry run whose stores all go to the sink (no branch in the loop).
         auto output = [&](int n, int pn) {
             const int par = n & 1;
-            f32x4 O[2][NRT];
+            f32x4 O[NCB][NRT];
 #pragma unroll
-            for (int b = 0; b < 2; ++b) {
+            for (int b = 0; b < NCB; ++b) {
                 Frag sf[NKS], uf[2];
 #pragma unroll
                 for (int ks = 0; ks < NKS; ++ks) sf[ks] = *reinterpret_cast<const Frag*>(&sSU[par][b][ks][lane][0]);
@@ -1715,7 +1738,7 @@ __global__ __launch_bounds__(320) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
             const int len = n < 0 ? 0 : chunk_len(n);
             const int64_t tok0 = tstart + (int64_t)n * C;
 #pragma unroll
-            for (int b = 0; b < 2; ++b)
+            for (int b = 0; b < NCB; ++b)
 #pragma unroll
                 for (int r = 0; r < NRT; ++r) {
                     const int tok = 16 * r + m;
@@ -1801,13 +1824,16 @@ void launch_trio(const PrefillArgs& a, const Plan& p, int npairs, int cus, int l
 
 // Five-wave scan: one workgroup per (pair, 32 columns), one per CU (its LDS
 // use, about 150 KB, keeps a second one off the CU).
-template <int DK, int DV>
+template <int DK, int DV, int NCB>
 void launch_quad(const PrefillArgs& a, const Plan& p, int npairs, hipStream_t stream) {
-    constexpr int NWG = DV / 32;
+    constexpr int NWG = DV / 16 / NCB;
     const bool varlen = a.cu_seqlens != nullptr;
     const int64_t groups = (npairs + 7) / 8;
     const unsigned grid = (unsigned)(groups * 8 * NWG);
-    hipLaunchKernelGGL((k2_quad_kernel<DK, DV>), dim3(grid), dim3(320), 0, stream,
+    // with one block per workgroup its LDS (~125 KB) already keeps a second
+    // workgroup off the CU; pad nothing
+    const unsigned pad = 0;
+    hipLaunchKernelGGL((k2_quad_kernel<DK, DV, NCB>), dim3(grid), dim3(64 * (NCB + 3)), pad, stream,
                        a.v, a.cu_seqlens, varlen ? p.order : nullptr,
                        varlen ? p.chunk_start : nullptr, varlen ? p.ckpt_base : nullptr, npairs,
                        a.total_tokens, a.H, p.max_chunks, p.handoff, a.initial_state, a.final_state,
@@ -1861,7 +1887,7 @@ hipError_t launch_typed(const PrefillArgs& a, hipStream_t stream) {
     if (scan) {
         switch (design) {
             case kTrio: launch_trio<DK, DV, 1>(a, p, npairs, cus, lds_max, stream); break;
-            case kQuad: launch_quad<DK, DV>(a, p, npairs, stream); break;
+            case kQuad: launch_quad<DK, DV, 2>(a, p, npairs, stream); break;
             case kNt4: launch_scan<DK, DV, 4, BF16>(a, p, npairs, stream); break;
             default: launch_scan<DK, DV, 1, BF16>(a, p, npairs, stream); break;
         }
