@@ -975,8 +975,8 @@ __global__ __launch_bounds__(kThreads) void k2_scan_kernel(
 // prefetches across the barriers. Blocks of Ab and P above the diagonal
 // (token rows 0-31, token slab 32-63) are zero and are neither loaded nor
 // multiplied.
-template <int DK, int DV, int NCB>
-__global__ __launch_bounds__(192 * NCB) __attribute__((amdgpu_waves_per_eu(1, 2))) void k2_trio_kernel(
+template <int DK, int DV>
+__global__ __launch_bounds__(192) __attribute__((amdgpu_waves_per_eu(1, 1))) void k2_trio_kernel(
     const void* vin, const int32_t* __restrict__ cu, const int32_t* __restrict__ order,
     const int32_t* __restrict__ chunk_start, const int32_t* __restrict__ ckpt_base, int npairs,
     int64_t N, int H, int64_t max_chunks, const unsigned char* handoff,
@@ -995,28 +995,18 @@ __global__ __launch_bounds__(192 * NCB) __attribute__((amdgpu_waves_per_eu(1, 2)
     constexpr int kLinesWg = (kLines + NVB - 1) / NVB;     // lines each column block touches
     constexpr int NTH = (kLinesWg + 63) / 64;              // handoff touches per lane
 
-    constexpr int NWG = NVB / NCB;  // workgroups per (seq, head)
-    static_assert(NVB % NCB == 0, "column blocks split evenly over workgroups");
+    __shared__ __attribute__((aligned(16))) E sV[2][64][8];             // V tile B-frags [slab] (swizzled rows)
+    __shared__ __attribute__((aligned(16))) f32x4 sU0[3][NRT][64];       // U0 = Ab V (result layout)
+    __shared__ __attribute__((aligned(16))) float sG[3][DK];             // Gamma_last
+    __shared__ __attribute__((aligned(16))) E sSU[2][NKS + 2][64][8];    // S(n) then U(n) fragments
 
-    // one set per column block of the workgroup
-    __shared__ __attribute__((aligned(16))) E sVs[NCB][2][64][8];            // V tile B-frags [slab]
-    __shared__ __attribute__((aligned(16))) f32x4 sU0s[NCB][3][NRT][64];      // U0 = Ab V (result layout)
-    __shared__ __attribute__((aligned(16))) float sGs[NCB][3][DK];            // Gamma_last
-    __shared__ __attribute__((aligned(16))) E sSUs[NCB][2][NKS + 2][64][8];   // S(n) then U(n) fragments
-
-    // wave roles: waves 0..NCB-1 run the chains (one SIMD each), then the
-    // output waves, then the preparation waves; cb = column block in the group
+    // wave 0 runs the chain, wave 1 the outputs, wave 2 the preparation
     const int wave = threadIdx.x >> 6;
-    const int role = wave / NCB, cb = wave % NCB;
-    auto& sV = sVs[cb];
-    auto& sU0 = sU0s[cb];
-    auto& sG = sGs[cb];
-    auto& sSU = sSUs[cb];
 
     const int id = blockIdx.x;
     const int xcd = id & 7, slot = id >> 3;
-    const int pair = xcd + 8 * (slot / NWG);
-    const int vb = (slot % NWG) * NCB + cb;
+    const int pair = xcd + 8 * (slot / NVB);
+    const int vb = slot % NVB;
     if (pair >= npairs) return;
     const int rank = pair / H, h = pair % H;
     const int seq = order ? order[rank] : rank;
@@ -1040,7 +1030,7 @@ __global__ __launch_bounds__(192 * NCB) __attribute__((amdgpu_waves_per_eu(1, 2)
     };
     const unsigned short* V = static_cast<const unsigned short*>(vin);
 
-    if (role == 0) {
+    if (wave == 0) {
         // ------------------------------------------------------ the chain ----
         Frag wn[NRT][NKS], kc[NST][2];
         auto load_w = [&](int n) {
@@ -1156,7 +1146,7 @@ __global__ __launch_bounds__(192 * NCB) __attribute__((amdgpu_waves_per_eu(1, 2)
             }
         }
         if (sfinal) store_state(sfinal + sbase);
-    } else if (role == 2) {
+    } else if (wave == 2) {
         // ------------------------------------------ next-chunk preparation ----
         // V: load instruction i covers rows 32 i + lane / 2, 16-byte half
         // lane % 2 of the row's 32-byte segment (two lanes per row)
@@ -1360,8 +1350,8 @@ __global__ __launch_bounds__(192 * NCB) __attribute__((amdgpu_waves_per_eu(1, 2)
 // every wave drains its prologue loads before its loop and issues each
 // loop's loads in a fixed order; the V and handoff pointers are not
 // __restrict__, which keeps prefetches from moving across the barriers.
-template <int DK, int DV, int NCB>
-__global__ __launch_bounds__(64 * (NCB + 3)) __attribute__((amdgpu_waves_per_eu(1, 2))) void k2_quad_kernel(
+template <int DK, int DV>
+__global__ __launch_bounds__(320) __attribute__((amdgpu_waves_per_eu(1, 2))) void k2_quad_kernel(
     const void* vin, const int32_t* __restrict__ cu, const int32_t* __restrict__ order,
     const int32_t* __restrict__ chunk_start, const int32_t* __restrict__ ckpt_base, int npairs,
     int64_t N, int H, int64_t max_chunks, const unsigned char* handoff,
@@ -1376,10 +1366,10 @@ __global__ __launch_bounds__(64 * (NCB + 3)) __attribute__((amdgpu_waves_per_eu(
     constexpr int NST = DK / 16;    // state row tiles
     constexpr int NRT = C / 16;     // token row tiles
     constexpr int NVB = DV / 16;    // column blocks per (seq, head)
+    constexpr int NCB = 2;          // column blocks per workgroup
     constexpr int NWG = NVB / NCB;  // workgroups per (seq, head)
     constexpr int LPR = 2 * NCB;    // prep: lanes per V row segment (16 bytes each)
     constexpr int RPI = 64 / LPR;   // prep: V rows per load instruction
-    static_assert(NVB % NCB == 0 && (NCB == 1 || NCB == 2), "one or two column blocks per workgroup");
     constexpr int NWF = NRT * NKS;  // W fragments per chunk
     constexpr int NKF = NST * 2;    // Kc^T fragments per chunk
     constexpr int kLines = (int)(HO::kBytes / 128);     // 128-byte lines per handoff block
@@ -1795,27 +1785,27 @@ void launch_scan(const PrefillArgs& a, const Plan& p, int npairs, hipStream_t st
                        a.ckpt_interval, a.ckpt_states, a.ckpt_rows, a.o, p.sink);
 }
 
-// Three-wave scan: one workgroup per (pair, 16 columns). When there are fewer
-// such workgroups than 4 per CU, each asks for enough (unused) LDS that at
-// most ceil(workgroups / CUs) of them share a CU, so they spread out instead
-// of queueing on one CU's vector memory path.
-template <int DK, int DV, int NCB>
+// Three-wave scan: one workgroup per (pair, 16 columns). When there are no
+// more such workgroups than CUs, each asks for enough (unused) LDS that no two
+// share a CU, so they spread out instead of queueing on one CU's vector
+// memory path.
+template <int DK, int DV>
 void launch_trio(const PrefillArgs& a, const Plan& p, int npairs, int cus, int lds_max,
                  hipStream_t stream) {
-    constexpr int NWG = DV / 16 / NCB;  // workgroups per (seq, head)
+    constexpr int NVB = DV / 16;  // workgroups per (seq, head)
     const bool varlen = a.cu_seqlens != nullptr;
     const int64_t groups = (npairs + 7) / 8;
-    const unsigned grid = (unsigned)(groups * 8 * NWG);
-    const int64_t wgs = (int64_t)npairs * NWG;
+    const unsigned grid = (unsigned)(groups * 8 * NVB);
+    const int64_t wgs = (int64_t)npairs * NVB;
     const int64_t per_cu = (wgs + cus - 1) / cus;
     unsigned pad = 0;
     hipFuncAttributes fa;
-    if (per_cu < 2 && hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(&k2_trio_kernel<DK, DV, NCB>)) == hipSuccess) {
+    if (per_cu < 2 && hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(&k2_trio_kernel<DK, DV>)) == hipSuccess) {
         const int64_t want = (int64_t)lds_max / per_cu - 512;
         const int64_t have = (int64_t)fa.sharedSizeBytes;
         pad = want > have ? (unsigned)(want - have) : 0u;
     }
-    hipLaunchKernelGGL((k2_trio_kernel<DK, DV, NCB>), dim3(grid), dim3(192 * NCB), pad, stream,
+    hipLaunchKernelGGL((k2_trio_kernel<DK, DV>), dim3(grid), dim3(192), pad, stream,
                        a.v, a.cu_seqlens, varlen ? p.order : nullptr,
                        varlen ? p.chunk_start : nullptr, varlen ? p.ckpt_base : nullptr, npairs,
                        a.total_tokens, a.H, p.max_chunks, p.handoff, a.initial_state, a.final_state,
@@ -1824,16 +1814,13 @@ void launch_trio(const PrefillArgs& a, const Plan& p, int npairs, int cus, int l
 
 // Five-wave scan: one workgroup per (pair, 32 columns), one per CU (its LDS
 // use, about 150 KB, keeps a second one off the CU).
-template <int DK, int DV, int NCB>
+template <int DK, int DV>
 void launch_quad(const PrefillArgs& a, const Plan& p, int npairs, hipStream_t stream) {
-    constexpr int NWG = DV / 16 / NCB;
+    constexpr int NWG = DV / 32;
     const bool varlen = a.cu_seqlens != nullptr;
     const int64_t groups = (npairs + 7) / 8;
     const unsigned grid = (unsigned)(groups * 8 * NWG);
-    // with one block per workgroup its LDS (~125 KB) already keeps a second
-    // workgroup off the CU; pad nothing
-    const unsigned pad = 0;
-    hipLaunchKernelGGL((k2_quad_kernel<DK, DV, NCB>), dim3(grid), dim3(64 * (NCB + 3)), pad, stream,
+    hipLaunchKernelGGL((k2_quad_kernel<DK, DV>), dim3(grid), dim3(320), 0, stream,
                        a.v, a.cu_seqlens, varlen ? p.order : nullptr,
                        varlen ? p.chunk_start : nullptr, varlen ? p.ckpt_base : nullptr, npairs,
                        a.total_tokens, a.H, p.max_chunks, p.handoff, a.initial_state, a.final_state,
@@ -1886,8 +1873,8 @@ hipError_t launch_typed(const PrefillArgs& a, hipStream_t stream) {
     }
     if (scan) {
         switch (design) {
-            case kTrio: launch_trio<DK, DV, 1>(a, p, npairs, cus, lds_max, stream); break;
-            case kQuad: launch_quad<DK, DV, 2>(a, p, npairs, stream); break;
+            case kTrio: launch_trio<DK, DV>(a, p, npairs, cus, lds_max, stream); break;
+            case kQuad: launch_quad<DK, DV>(a, p, npairs, stream); break;
             case kNt4: launch_scan<DK, DV, 4, BF16>(a, p, npairs, stream); break;
             default: launch_scan<DK, DV, 1, BF16>(a, p, npairs, stream); break;
         }
