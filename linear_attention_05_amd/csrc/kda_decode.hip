@@ -9,14 +9,22 @@
 // fp32 state traffic per head and token (Kimi K3 report, "Key data"): under
 // one FLOP per byte, so the kernel is built for HBM bandwidth, with no MFMA.
 //
-// Mapping: one 256-thread workgroup per (b, h). Thread t owns the 4 adjacent
+// Mapping: one 512-thread workgroup per (b, h). Thread t owns the 4 adjacent
 // value columns 4*(t % CG) .. +3 (CG = Dv/4) of the key rows
-// rg, rg + RG, rg + 2*RG, ... (rg = t / CG, RG = 256/CG): one wave reads
+// rg, rg + RG, rg + 2*RG, ... (rg = t / CG, RG = 512/CG): one wave reads
 // 64/CG whole adjacent rows per 16-byte-per-lane load, so each load
 // instruction moves 1 KiB of contiguous state. The decayed slab stays in
 // VGPRs between the reduction and the write-back; r, p and k.q are reduced
-// across row groups with lane shuffles and then across the 4 waves in LDS, in
+// across row groups with lane shuffles and then across the 8 waves in LDS, in
 // a fixed order (bitwise reproducible).
+//
+// Residency: HBM sustains this read-then-write stream best with few state
+// blocks in flight per CU. Measured on MI355X for 64 KiB states
+// (B = 512, H = 32, D = 128): one 512-thread workgroup per CU moves
+// 6.1-6.2 TB/s; two per CU 5.8; the default residency (four) 5.4; 256-thread
+// workgroups 5.4-5.55 at any residency. The launch therefore asks for enough
+// (unused) dynamic LDS that only n workgroups fit on a CU, n = 64 KiB / state
+// bytes (at least 1), keeping about 64 KiB of state in flight per CU.
 #include "kda_internal.h"
 
 namespace kda {
@@ -47,7 +55,7 @@ __device__ __forceinline__ f32x4 load_in4(const void* p, int64_t i) {
     }
 }
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
 
 template <int DK, int DV, bool BF16>
@@ -145,16 +153,38 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
     }
 }
 
+// Dynamic LDS (never touched by the kernel) that leaves room for only
+// n = max(1, 64 KiB / state bytes) decode workgroups per CU: each asks for
+// lds_per_cu / (n + 1/2) bytes in all, more than a share of n + 1 and no
+// more than a share of n.
+template <int DK, int DV>
+unsigned residency_pad() {
+    constexpr int CG = DV / 4;
+    constexpr int kStatic = 3 * DK * 4 + kWaves * CG * 2 * 16 + kWaves * 4;
+    const int n = (DK * DV * 4 >= 65536) ? 1 : 65536 / (DK * DV * 4);
+    int lds = 0, dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) != hipSuccess || lds <= 0)
+        return 0;
+    int per_block = 0;
+    if (hipDeviceGetAttribute(&per_block, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
+        return 0;
+    const int64_t want = (int64_t)lds * 2 / (2 * n + 1) - kStatic;
+    if (want <= 0 || want + kStatic > per_block) return 0;  // cannot pad: default residency
+    return (unsigned)want;
+}
+
 template <int DK, int DV>
 hipError_t launch_dims(const void* q, const void* k, const void* v, bool bf16, const float* g,
                        const float* beta, int B, int H, float* state, float* o,
                        hipStream_t stream) {
     const dim3 grid((unsigned)((int64_t)B * H)), block(kThreads);
+    const unsigned pad = residency_pad<DK, DV>();
     if (bf16)
-        hipLaunchKernelGGL((decode_kernel<DK, DV, true>), grid, block, 0, stream, q, k, v, g,
+        hipLaunchKernelGGL((decode_kernel<DK, DV, true>), grid, block, pad, stream, q, k, v, g,
                            beta, state, o);
     else
-        hipLaunchKernelGGL((decode_kernel<DK, DV, false>), grid, block, 0, stream, q, k, v, g,
+        hipLaunchKernelGGL((decode_kernel<DK, DV, false>), grid, block, pad, stream, q, k, v, g,
                            beta, state, o);
     return hipGetLastError();
 }
