@@ -26,6 +26,7 @@ sys.path.insert(0, ROOT)
 PREFILL_WORKLOAD = 1
 DECODE_WORKLOAD = 4
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+MFMA_FILE = os.path.join(ROOT, "profiles", "mfma.json")
 
 
 def kernel_source_sha() -> str:
@@ -51,6 +52,21 @@ def measured_traffic(kernel: str):
     if not k:
         return None
     return k.get("fetch_bytes", 0) + k.get("write_bytes", 0)
+
+
+def measured_mfma(kernel: str):
+    """Matrix-core utilisation of a kernel from rocprofv3 counters
+    (profiles/mfma.json): busy cycles over active cycles x SIMDs, and the MFMA
+    FLOPs the counters saw per launch; None when absent or taken on different
+    kernel sources."""
+    try:
+        with open(MFMA_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    return t.get("kernels", {}).get(kernel)
 
 
 def dev(arr):
@@ -260,6 +276,9 @@ def main():
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run one device-to-device copy of this many MiB (a known-size "
                          "reference dispatch for hardware traffic counters)")
+    ap.add_argument("--mfma-calibration", action="store_true",
+                    help="first run one fp16 8192^3 GEMM (a known-FLOP reference dispatch for "
+                         "matrix-core counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -284,6 +303,14 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    if args.mfma_calibration:
+        a = torch.randn(8192, 8192, device="cuda", dtype=torch.float16)
+        b = torch.randn(8192, 8192, device="cuda", dtype=torch.float16)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            torch.mm(a, b)
+        torch.cuda.synchronize()
+        del a, b
 
     out = {}
     if args.only in ("all", "prefill"):
@@ -310,8 +337,10 @@ def main():
                 "flops_per_step": p["flops"],
                 "path_compulsory_bytes": p["compulsory_bytes"],
                 "path_roofline_frac": round(p["compulsory_bytes"] / (step_ms * 1e-3) / 8e12, 4),
-                "k1_prep": dict(k1, ms=round(p["k1_ms"], 4), bytes=p["k1_bytes"]),
-                "k2_scan": dict(k2, ms=round(p["k2_ms"], 4), bytes=p["k2_bytes"]),
+                "k1_prep": dict(k1, ms=round(p["k1_ms"], 4), bytes=p["k1_bytes"],
+                                mfma=measured_mfma("k1_prep")),
+                "k2_scan": dict(k2, ms=round(p["k2_ms"], 4), bytes=p["k2_bytes"],
+                                mfma=measured_mfma("k2_scan")),
             },
         })
     if args.only in ("all", "decode"):
