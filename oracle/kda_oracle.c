@@ -26,8 +26,9 @@
  * the explicit matrix form above is the reading taken here.
  *
  * Readings where the pages are silent: no attention scale; q and k are used
- * exactly as given (the caller L2-normalises them); g = log(alpha) is the
- * input; a checkpoint is a copy of S after every ckpt_interval tokens of a
+ * exactly as given (the caller L2-normalises them; oracle/frontend.py holds
+ * the parameter-free input transforms, applied in fp64 before this file's
+ * recurrence when the inputs are raw); g = log(alpha) is the input; a checkpoint is a copy of S after every ckpt_interval tokens of a
  * sequence; a zero-length sequence returns its initial state.
  *
  * Columns of S (value channels) never interact, so a work unit is
@@ -44,9 +45,12 @@
 
 #define ORC_F32 0
 #define ORC_BF16 1
+#define ORC_F64 2 /* every input (q, k, v, g, beta) is fp64 */
 
 static double in_val(const void *p, int dtype, int64_t i)
 {
+    if (dtype == ORC_F64)
+        return ((const double *)p)[i];
     if (dtype == ORC_F32)
         return (double)((const float *)p)[i];
     uint32_t u = (uint32_t)((const uint16_t *)p)[i] << 16;
@@ -55,14 +59,20 @@ static double in_val(const void *p, int dtype, int64_t i)
     return (double)f;
 }
 
+/* g and beta: fp64 with ORC_F64 inputs, fp32 otherwise. */
+static double gb_val(const void *p, int dtype, int64_t i)
+{
+    return dtype == ORC_F64 ? ((const double *)p)[i] : (double)((const float *)p)[i];
+}
+
 /* One token on columns [j0, j0 + nc) of S (row-major Dk x nc, fp64). */
 static void token_step(double *S, int Dk, int nc, int j0,
                        const void *q, const void *k, const void *v, int dtype,
-                       int64_t qk_off, int64_t v_off, const float *g, double beta,
+                       int64_t qk_off, int64_t v_off, const void *g, double beta,
                        double *kv, double *qv, double *u, double *o_out /* nc or NULL */)
 {
     for (int i = 0; i < Dk; ++i) {
-        double a = exp((double)g[qk_off + i]);
+        double a = exp(gb_val(g, dtype, qk_off + i));
         kv[i] = in_val(k, dtype, qk_off + i);
         qv[i] = in_val(q, dtype, qk_off + i);
         double *row = S + (int64_t)i * nc;
@@ -104,8 +114,8 @@ static int set_threads(int n_threads)
 
 /*
  * Prefill over packed sequences.
- *   q, k [N, H, Dk], v [N, H, Dv]  fp32 or bf16 bits (dtype)
- *   g [N, H, Dk] fp32, beta [N, H] fp32
+ *   q, k [N, H, Dk], v [N, H, Dv]  fp32 or bf16 bits (dtype), or fp64
+ *   g [N, H, Dk], beta [N, H]  fp32 (fp64 when dtype is ORC_F64)
  *   cu_seqlens [num_seqs + 1] (int64), packed token offsets
  *   initial_state [num_seqs, H, Dk, Dv] fp32 or NULL (zeros)
  *   final_state   [num_seqs, H, Dk, Dv] fp64 or NULL
@@ -116,7 +126,7 @@ static int set_threads(int n_threads)
  * Returns 0, or -1 on bad arguments / allocation failure.
  */
 int kda_oracle_prefill(const void *q, const void *k, const void *v, int dtype,
-                       const float *g, const float *beta,
+                       const void *g, const void *beta,
                        const int64_t *cu_seqlens, int num_seqs, int H, int Dk, int Dv,
                        const float *initial_state, double *final_state,
                        int64_t ckpt_interval, double *ckpt, double *o,
@@ -181,7 +191,7 @@ int kda_oracle_prefill(const void *q, const void *k, const void *v, int dtype,
                     int64_t qk_off = (t * H + h) * (int64_t)Dk;
                     int64_t v_off = (t * H + h) * (int64_t)Dv;
                     token_step(S, Dk, nc, j0, q, k, v, dtype, qk_off, v_off, g,
-                               (double)beta[t * H + h], kv, qv, u, ob);
+                               gb_val(beta, dtype, t * H + h), kv, qv, u, ob);
                     for (int j = 0; j < nc; ++j)
                         o[v_off + j0 + j] = ob[j];
                     int64_t done = t + 1 - t0;
@@ -213,11 +223,12 @@ int kda_oracle_prefill(const void *q, const void *k, const void *v, int dtype,
 /*
  * One decode step for B independent sequences: the same token body on an
  * fp64 state [B, H, Dk, Dv] that is read and updated in place.
- *   q, k [B, H, Dk], v [B, H, Dv] (dtype), g [B, H, Dk], beta [B, H], o [B, H, Dv] fp64.
+ *   q, k [B, H, Dk], v [B, H, Dv] (dtype), g [B, H, Dk], beta [B, H] (fp32, or
+ *   fp64 when dtype is ORC_F64), o [B, H, Dv] fp64.
  *   units: (batch, head, column block) triples or NULL for all.
  */
 int kda_oracle_decode(const void *q, const void *k, const void *v, int dtype,
-                      const float *g, const float *beta, int B, int H, int Dk, int Dv,
+                      const void *g, const void *beta, int B, int H, int Dk, int Dv,
                       double *state, double *o, const int32_t *units, int64_t n_units,
                       int col_block, int n_threads)
 {
@@ -264,7 +275,7 @@ int kda_oracle_decode(const void *q, const void *k, const void *v, int dtype,
                 int64_t qk_off = ((int64_t)b * H + h) * Dk;
                 int64_t v_off = ((int64_t)b * H + h) * Dv;
                 token_step(S, Dk, nc, j0, q, k, v, dtype, qk_off, v_off, g,
-                           (double)beta[(int64_t)b * H + h], kv, qv, u, ob);
+                           gb_val(beta, dtype, (int64_t)b * H + h), kv, qv, u, ob);
                 for (int j = 0; j < nc; ++j)
                     o[v_off + j0 + j] = ob[j];
                 for (int i = 0; i < Dk; ++i)

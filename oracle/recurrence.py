@@ -14,7 +14,7 @@ import numpy as np
 from . import build as _build
 
 _LIB = None
-F32, BF16 = 0, 1
+F32, BF16, F64 = 0, 1, 2
 
 
 def load(path):
@@ -54,7 +54,14 @@ def _dtype_code(arr):
         return BF16
     if arr.dtype == np.float32:
         return F32
-    raise TypeError(f"q/k/v must be float32 or uint16 bf16 bits, got {arr.dtype}")
+    if arr.dtype == np.float64:
+        return F64
+    raise TypeError(f"q/k/v must be float32, float64 or uint16 bf16 bits, got {arr.dtype}")
+
+
+def _gb(x, dt):
+    """g and beta travel as fp64 with fp64 q/k/v, as fp32 otherwise."""
+    return np.ascontiguousarray(x, dtype=np.float64 if dt == F64 else np.float32)
 
 
 def num_threads(n: int = 0) -> int:
@@ -67,8 +74,9 @@ def prefill(q, k, v, g, beta, cu_seqlens, *, initial_state=None, ckpt_interval=0
             lib=None):
     """Run the recurrence over packed sequences.
 
-    q, k: [N, H, Dk]; v: [N, H, Dv] (float32 or uint16 bf16 bits, same dtype);
-    g: [N, H, Dk] float32; beta: [N, H] float32; cu_seqlens: [num_seqs + 1].
+    q, k: [N, H, Dk]; v: [N, H, Dv] (float32, uint16 bf16 bits or float64, one dtype);
+    g: [N, H, Dk]; beta: [N, H] (float32; float64 when q/k/v are float64);
+    cu_seqlens: [num_seqs + 1].
     initial_state: [num_seqs, H, Dk, Dv] float32 or None (zeros).
     units: optional int array [n, 3] of (seq, head, column block) to compute;
     outputs of other units stay NaN.
@@ -78,8 +86,8 @@ def prefill(q, k, v, g, beta, cu_seqlens, *, initial_state=None, ckpt_interval=0
     dt = _dtype_code(q)
     if _dtype_code(k) != dt or _dtype_code(v) != dt:
         raise TypeError("q, k, v must share one dtype")
-    g = np.ascontiguousarray(g, dtype=np.float32)
-    beta = np.ascontiguousarray(beta, dtype=np.float32)
+    g = _gb(g, dt)
+    beta = _gb(beta, dt)
     cu = np.ascontiguousarray(cu_seqlens, dtype=np.int64)
     N, H, Dk = q.shape
     Dv = v.shape[2]
@@ -118,8 +126,8 @@ def decode(q, k, v, g, beta, state, *, units=None, col_block=16, n_threads=0, li
     Returns o [B, H, Dv] float64 (NaN outside the listed units)."""
     q = np.ascontiguousarray(q); k = np.ascontiguousarray(k); v = np.ascontiguousarray(v)
     dt = _dtype_code(q)
-    g = np.ascontiguousarray(g, dtype=np.float32)
-    beta = np.ascontiguousarray(beta, dtype=np.float32)
+    g = _gb(g, dt)
+    beta = _gb(beta, dt)
     if state.dtype != np.float64 or not state.flags.c_contiguous:
         raise TypeError("state must be a C-contiguous float64 array")
     B, H, Dk = q.shape

@@ -15,6 +15,11 @@ Distributions (one recipe for every workload):
   * initial recurrent states ~ N(0, 0.02) (standard deviation 0.02), fp32.
   * N(mu, s) always names the standard deviation s.
 
+Raw variant (raw=True, for the library's in-kernel front-end): the same
+streams with the last step of each recipe left out -- q, k ~ N(0, 1) cast
+to the storage dtype without normalisation, g holds u itself (fp32) and beta
+holds x itself (fp32).
+
 Casting: fp64 -> fp32 with round-to-nearest-even (numpy astype); bf16 tensors
 are then rounded fp32 -> bf16 with round-to-nearest-even and are returned as
 raw uint16 bit patterns.
@@ -117,6 +122,23 @@ def draw_qk(n_tok, H, D, seed, tag, dtype):
                          lambda r, nb: to_storage(_unit_rows(r, nb, H, D), dtype), st)
 
 
+def draw_qk_raw(n_tok, H, D, seed, tag, dtype):
+    st = np.uint16 if dtype == "bf16" else np.float32
+    return _fill_blocked((H, D), n_tok, seed, tag,
+                         lambda r, nb: to_storage(r.standard_normal((nb, H, D)), dtype), st)
+
+
+def draw_u(n_tok, H, D, seed, tag=TAG_U):
+    return _fill_blocked((H, D), n_tok, seed, tag,
+                         lambda r, nb: r.normal(DECAY_MU, DECAY_SIGMA, size=(nb, H, D)).astype(np.float32),
+                         np.float32)
+
+
+def draw_beta_logits(n_tok, H, seed, tag=TAG_B):
+    return _fill_blocked((H,), n_tok, seed, tag,
+                         lambda r, nb: r.standard_normal((nb, H)).astype(np.float32), np.float32)
+
+
 def draw_v(n_tok, H, D, seed, dtype, tag=TAG_V):
     st = np.uint16 if dtype == "bf16" else np.float32
     return _fill_blocked((H, D), n_tok, seed, tag,
@@ -200,14 +222,21 @@ class PrefillInputs:
 
 
 def make_prefill(lengths, H, Dk, Dv, dtype, seed, *, init_state=True,
-                 ckpt_interval=0, chunk_size=64, name="") -> PrefillInputs:
+                 ckpt_interval=0, chunk_size=64, name="", raw=False) -> PrefillInputs:
+    """raw=True: q, k un-normalised, g = u and beta = x (see the module notes)."""
     lengths = [int(L) for L in lengths]
     n_tok = sum(lengths)
-    q = draw_qk(n_tok, H, Dk, seed, TAG_Q, dtype)
-    k = draw_qk(n_tok, H, Dk, seed, TAG_K, dtype)
+    if raw:
+        q = draw_qk_raw(n_tok, H, Dk, seed, TAG_Q, dtype)
+        k = draw_qk_raw(n_tok, H, Dk, seed, TAG_K, dtype)
+        g = draw_u(n_tok, H, Dk, seed)
+        beta = draw_beta_logits(n_tok, H, seed)
+    else:
+        q = draw_qk(n_tok, H, Dk, seed, TAG_Q, dtype)
+        k = draw_qk(n_tok, H, Dk, seed, TAG_K, dtype)
+        g = draw_g(n_tok, H, Dk, seed)
+        beta = draw_beta(n_tok, H, seed)
     v = draw_v(n_tok, H, Dv, seed, dtype)
-    g = draw_g(n_tok, H, Dk, seed)
-    beta = draw_beta(n_tok, H, seed)
     s0 = draw_states(len(lengths), H, Dk, Dv, seed) if init_state else None
     return PrefillInputs(dtype, H, Dk, Dv, lengths, q, k, v, g, beta, s0,
                          ckpt_interval=ckpt_interval, chunk_size=chunk_size,
@@ -270,15 +299,22 @@ def decode_state(B, H, Dk, Dv, seed) -> np.ndarray:
     return draw_states(B, H, Dk, Dv, seed)
 
 
-def decode_step_inputs(B, H, Dk, Dv, dtype, seed, step) -> DecodeStep:
+def decode_step_inputs(B, H, Dk, Dv, dtype, seed, step, raw=False) -> DecodeStep:
     """Inputs of one decode step: [B, H, D] tensors; the step index selects
-    the stream block, so steps are independent draws."""
+    the stream block, so steps are independent draws. raw=True as in
+    make_prefill."""
     def one(tag, fn):
         rng = np.random.default_rng([seed, tag, 1_000_000 + step])
         return fn(rng)
-    q = one(TAG_Q, lambda r: to_storage(_unit_rows(r, B, H, Dk), dtype))
-    k = one(TAG_K, lambda r: to_storage(_unit_rows(r, B, H, Dk), dtype))
+    if raw:
+        q = one(TAG_Q, lambda r: to_storage(r.standard_normal((B, H, Dk)), dtype))
+        k = one(TAG_K, lambda r: to_storage(r.standard_normal((B, H, Dk)), dtype))
+        g = one(TAG_U, lambda r: r.normal(DECAY_MU, DECAY_SIGMA, size=(B, H, Dk)).astype(np.float32))
+        beta = one(TAG_B, lambda r: r.standard_normal((B, H)).astype(np.float32))
+    else:
+        q = one(TAG_Q, lambda r: to_storage(_unit_rows(r, B, H, Dk), dtype))
+        k = one(TAG_K, lambda r: to_storage(_unit_rows(r, B, H, Dk), dtype))
+        g = one(TAG_U, lambda r: (-np.exp(r.normal(DECAY_MU, DECAY_SIGMA, size=(B, H, Dk)))).astype(np.float32))
+        beta = one(TAG_B, lambda r: (1.0 / (1.0 + np.exp(-r.standard_normal((B, H))))).astype(np.float32))
     v = one(TAG_V, lambda r: to_storage(r.standard_normal((B, H, Dv)), dtype))
-    g = one(TAG_U, lambda r: (-np.exp(r.normal(DECAY_MU, DECAY_SIGMA, size=(B, H, Dk)))).astype(np.float32))
-    beta = one(TAG_B, lambda r: (1.0 / (1.0 + np.exp(-r.standard_normal((B, H))))).astype(np.float32))
     return DecodeStep(q, k, v, g, beta)
