@@ -28,7 +28,7 @@ MUTANTS = {
     "readout_transposed": ("acc += S[(int64_t)i * nc + j] * qv[i];",
                            "acc += S[(int64_t)(j % Dk) * nc + (i % nc)] * qv[i];"),
     "write_with_query": ("row[j] += kv[i] * u[j];", "row[j] += qv[i] * u[j];"),
-    "decay_after_write_partial": ("exp((double)g[qk_off + i])", "exp(0.5 * (double)g[qk_off + i])"),
+    "decay_after_write_partial": ("exp(gb_val(g, dtype, qk_off + i))", "exp(0.5 * gb_val(g, dtype, qk_off + i))"),
 }
 
 
