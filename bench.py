@@ -232,6 +232,98 @@ def bench_prefill_workload(idx, reps=3):
                 path_roofline_frac=round(byts / (ms * 1e-3) / 8e12, 4))
 
 
+def bench_frontend(steps=10, warmup=3, decode_steps=32):
+    """The in-kernel parameter-free front-end (KDA_FRONT_*: q/k L2 normalisation,
+    g = -exp(u), sigmoid write strength) on raw inputs of the headline prefill
+    and decode shapes, beside what the same transforms cost as separate torch
+    passes before the plain path."""
+    import numpy as np
+    import torch
+    import linear_attention_05_amd as K
+    from linear_attention_05_amd import _binding as B
+    from synth import (WORKLOADS, decode_state, decode_step_inputs, make_prefill,
+                       workload_lengths, workload_seed)
+
+    w = WORKLOADS[PREFILL_WORKLOAD]
+    x = make_prefill(workload_lengths(PREFILL_WORKLOAD), w["H"], w["D"], w["D"], w["dtype"],
+                     workload_seed(PREFILL_WORKLOAD), raw=True)
+    N, H, D = x.total_tokens, x.H, x.Dk
+    q, k, v, u, b, s0 = (dev(a) for a in (x.q, x.k, x.v, x.g, x.beta, x.initial_state))
+    o = torch.empty(N, H, D, device="cuda")
+    fs = torch.empty(1, H, D, D, device="cuda")
+    ws = torch.empty(K.kda_prefill_workspace_size(N, 1, H, D, D), dtype=torch.uint8, device="cuda")
+
+    def phase(p):
+        K.kda_prefill_chunked(q, k, v, u, b, initial_state=s0, final_state=fs, o=o,
+                              workspace=ws, phases=p, frontend=B.FRONT_ALL)
+
+    def prepass():  # the same transforms as separate passes (bf16 q/k written back)
+        qn = (q.float() * torch.rsqrt(q.float().square().sum(-1, keepdim=True) + 1e-6)).bfloat16()
+        kn = (k.float() * torch.rsqrt(k.float().square().sum(-1, keepdim=True) + 1e-6)).bfloat16()
+        return qn, kn, -torch.exp(u), torch.sigmoid(b)
+
+    for _ in range(warmup):
+        phase(B.PHASE_PREPARE)
+        phase(B.PHASE_SCAN)
+        prepass()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        ev[i][0].record()
+        phase(B.PHASE_PREPARE)
+        ev[i][1].record()
+        phase(B.PHASE_SCAN)
+        ev[i][2].record()
+        prepass()
+        ev[i][3].record()
+    torch.cuda.synchronize()
+    k1 = float(np.median([e[0].elapsed_time(e[1]) for e in ev]))
+    k2 = float(np.median([e[1].elapsed_time(e[2]) for e in ev]))
+    pre = float(np.median([e[2].elapsed_time(e[3]) for e in ev]))
+    del q, k, v, u, b, o, ws
+
+    # decode: plain and front-end steps interleaved on one state, so both see
+    # the same memory
+    wd = WORKLOADS[DECODE_WORKLOAD]
+    Bsz, Hd, Dd = wd["B"], wd["H"], wd["D"]
+    seed = workload_seed(DECODE_WORKLOAD)
+    state = dev(decode_state(Bsz, Hd, Dd, Dd, seed))
+    raw = [tuple(dev(a) for a in (s.q, s.k, s.v, s.g, s.beta))
+           for s in (decode_step_inputs(Bsz, Hd, Dd, Dd, wd["dtype"], seed, t, raw=True)
+                     for t in range(decode_steps))]
+    plain = [tuple(dev(a) for a in (s.q, s.k, s.v, s.g, s.beta))
+             for s in (decode_step_inputs(Bsz, Hd, Dd, Dd, wd["dtype"], seed, t)
+                       for t in range(decode_steps))]
+    od = torch.empty(Bsz, Hd, Dd, device="cuda")
+    for i in range(2 * warmup):
+        K.kda_decode_step(*plain[i % decode_steps], state, od)
+        K.kda_decode_step(*raw[i % decode_steps], state, od, frontend=B.FRONT_ALL)
+    evd = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(decode_steps)]
+    torch.cuda.synchronize()
+    for i in range(decode_steps):
+        evd[i][0].record()
+        K.kda_decode_step(*plain[i], state, od)
+        evd[i][1].record()
+        K.kda_decode_step(*raw[i], state, od, frontend=B.FRONT_ALL)
+        evd[i][2].record()
+    torch.cuda.synchronize()
+    dec_plain = float(np.median([e[0].elapsed_time(e[1]) for e in evd]))
+    dec_ms = float(np.median([e[1].elapsed_time(e[2]) for e in evd]))
+    from linear_attention_05_amd import accounting as acc
+    dec_bytes = Bsz * Hd * acc.decode_bytes_per_head_token(Dd, Dd, 2)
+    return dict(
+        transforms="q/k L2 norm, g=-exp(u), beta=sigmoid(b), inside the kernels (raw inputs)",
+        prefill_workload=f"B=1 T={N} H={H} D={D} bf16",
+        prefill_k1_ms=round(k1, 4), prefill_k2_ms=round(k2, 4),
+        prefill_ms=round(k1 + k2, 4), prefill_mtok_s=round(N / ((k1 + k2) * 1e-3) / 1e6, 3),
+        torch_prepass_ms=round(pre, 4),
+        decode_workload=f"B={Bsz} H={Hd} D={Dd} bf16, {decode_steps} steps, each beside a "
+                        "plain step on the same state",
+        decode_us_per_step=round(dec_ms * 1e3, 2),
+        decode_gbps=round(dec_bytes / (dec_ms * 1e-3) / 1e9, 1),
+        decode_plain_us_per_step=round(dec_plain * 1e3, 2))
+
+
 def hbm_ceilings():
     """Practical HBM rates of plain torch kernels on 1 GiB (context for the
     roofline fractions): read-only (sum), write-only (fill), copy (read+write)."""
@@ -362,6 +454,7 @@ def main():
     if args.only in ("all", "prefill") and not args.no_extra_workloads:
         out["prefill_workloads"] = [bench_prefill_workload(2), bench_prefill_workload(3)]
     if args.only == "all" and not args.no_extra_workloads:
+        out["frontend"] = bench_frontend()
         out["hbm_ceilings"] = hbm_ceilings()
     if args.only in ("all", "prefill") and not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(p["inputs"])

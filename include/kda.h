@@ -33,6 +33,8 @@
  *     g, beta, states and o are always fp32.
  *   - q and k are expected to be L2-normalised per (token, head) by the
  *     caller; the library uses them as given and applies no attention scale.
+ *     The *_ex entry points can instead apply KDA's parameter-free input
+ *     transforms themselves (KDA_FRONT_* below).
  *   - Tensor pointers must be 16-byte aligned; workspace 256-byte aligned.
  *   - Arguments are validated on the host BEFORE any HIP call. On any error
  *     nothing is enqueued and no output is touched, except KDA_ERR_HIP, which
@@ -164,6 +166,43 @@ kda_status_t kda_prefill_chunked_phases(
     void *workspace, size_t workspace_bytes, uint32_t phases, hipStream_t stream);
 
 /*
+ * Parameter-free input transforms applied inside the kernels: bit mask
+ * `frontend` of kda_prefill_chunked_ex and kda_decode_step_ex. KDA normalises
+ * queries and keys to unit L2 norm and drives its per-channel decay through a
+ * gate (Kimi K3 report, "Methodology notes", Kimi Delta Attention bullet);
+ * the pages give no formulas, and these are the library's reading:
+ *   KDA_FRONT_L2NORM_QK     every q and k row (one token, one head) is scaled
+ *                           by 1 / sqrt(sum_c x_c^2 + 1e-6), in fp32, where it
+ *                           enters the computation (a zero row stays zero)
+ *   KDA_FRONT_GATE          g holds u; the log-decay used is -exp(u)
+ *   KDA_FRONT_BETA_SIGMOID  beta holds logits b; the write strength used is
+ *                           1 / (1 + exp(-b))
+ * Tensors keep their shapes, dtypes and layouts, and are only read. The
+ * weighted parts of KDA's input path (short convolution, low-rank gate
+ * projection, output gate) are the caller's.
+ */
+#define KDA_FRONT_L2NORM_QK 1u
+#define KDA_FRONT_GATE 2u
+#define KDA_FRONT_BETA_SIGMOID 4u
+
+/*
+ * kda_prefill_chunked_phases with a `frontend` mask (a subset of the
+ * KDA_FRONT_* bits; 0 = kda_prefill_chunked_phases). The transforms act in
+ * the PREPARE phase, the only one that reads q, k, g and beta; a SCAN-only
+ * call ignores them. The documented decay precondition then applies to
+ * -exp(u). Returns KDA_ERR_INVALID_ARG for unknown bits, otherwise as
+ * kda_prefill_chunked_phases.
+ */
+kda_status_t kda_prefill_chunked_ex(
+    const void *q, const void *k, const void *v, kda_dtype_t in_dtype,
+    const float *g, const float *beta, const int32_t *cu_seqlens,
+    int32_t num_seqs, int64_t total_tokens, int32_t H, int32_t Dk, int32_t Dv,
+    int32_t chunk_size, const float *initial_state, float *final_state,
+    int64_t ckpt_interval, float *ckpt_states, int64_t ckpt_rows, float *o,
+    void *workspace, size_t workspace_bytes, uint32_t phases, uint32_t frontend,
+    hipStream_t stream);
+
+/*
  * One KDA decode step for B independent sequences (one new token each).
  *
  * For each (b, h): S <- (I - beta k k^T) Diag(exp(g)) S + beta k v^T and
@@ -182,6 +221,16 @@ kda_status_t kda_decode_step(
     const void *q, const void *k, const void *v, kda_dtype_t in_dtype,
     const float *g, const float *beta, int32_t B, int32_t H, int32_t Dk, int32_t Dv,
     float *state, float *o, hipStream_t stream);
+
+/*
+ * kda_decode_step with a `frontend` mask (a subset of the KDA_FRONT_* bits;
+ * 0 = kda_decode_step). Returns KDA_ERR_INVALID_ARG for unknown bits,
+ * otherwise as kda_decode_step.
+ */
+kda_status_t kda_decode_step_ex(
+    const void *q, const void *k, const void *v, kda_dtype_t in_dtype,
+    const float *g, const float *beta, int32_t B, int32_t H, int32_t Dk, int32_t Dv,
+    float *state, float *o, uint32_t frontend, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -53,7 +53,7 @@ def kda_prefill_workspace_size(total_tokens, num_seqs, H, Dk, Dv, dtype=torch.bf
 def kda_prefill_chunked(q, k, v, g, beta, *, cu_seqlens=None, num_seqs=None,
                         initial_state=None, output_final_state=True, final_state=None,
                         ckpt_interval=0, num_checkpoints=None, ckpt_states=None, o=None,
-                        workspace=None, phases=B.PHASE_PREPARE | B.PHASE_SCAN):
+                        workspace=None, phases=B.PHASE_PREPARE | B.PHASE_SCAN, frontend=0):
     """Chunked KDA prefill (see include/kda.h, kda_prefill_chunked).
 
     q, k [N, H, Dk], v [N, H, Dv] (bf16 or fp32, one dtype); g [N, H, Dk] fp32;
@@ -62,6 +62,9 @@ def kda_prefill_chunked(q, k, v, g, beta, *, cu_seqlens=None, num_seqs=None,
     floor(L_s / ckpt_interval)) or a preallocated ckpt_states.
     phases selects prepare (K1), scan (K2) or both (kda_prefill_chunked_phases);
     a scan-only call must reuse the workspace of a preceding prepare.
+    frontend: KDA_FRONT_* bits (FRONT_L2NORM_QK, FRONT_GATE, FRONT_BETA_SIGMOID)
+    applied inside the kernels to raw q/k, g (= u) and beta (= logits)
+    (kda_prefill_chunked_ex); 0 uses the inputs as given.
     Returns (o, final_state or None, ckpt_states or None)."""
     dev = q.device
     N, H, Dk = q.shape
@@ -100,18 +103,21 @@ def kda_prefill_chunked(q, k, v, g, beta, *, cu_seqlens=None, num_seqs=None,
     if ckpt_interval > 0 and ckpt_states.numel() == 0:
         # zero checkpoint rows: any aligned non-null pointer is never written
         ck_ptr = workspace.data_ptr()
-    st = B.prefill_phases_raw(_ptr(q), _ptr(k), _ptr(v), code, _ptr(g), _ptr(beta),
-                              _ptr(cu_seqlens), num_seqs, N, H, Dk, Dv, CHUNK,
-                              _ptr(initial_state), _ptr(final_state), int(ckpt_interval), ck_ptr,
-                              ck_rows, _ptr(o), _ptr(workspace), workspace.numel(), int(phases),
-                              _stream(dev))
+    args = (_ptr(q), _ptr(k), _ptr(v), code, _ptr(g), _ptr(beta), _ptr(cu_seqlens), num_seqs, N,
+            H, Dk, Dv, CHUNK, _ptr(initial_state), _ptr(final_state), int(ckpt_interval), ck_ptr,
+            ck_rows, _ptr(o), _ptr(workspace), workspace.numel(), int(phases))
+    if frontend:
+        st = B.prefill_ex_raw(*args, int(frontend), _stream(dev))
+    else:
+        st = B.prefill_phases_raw(*args, _stream(dev))
     if st != B.KDA_OK:
         raise B.KdaError(st, "kda_prefill_chunked")
     return o, final_state, ckpt_states
 
 
-def kda_decode_step(q, k, v, g, beta, state, o=None):
+def kda_decode_step(q, k, v, g, beta, state, o=None, frontend=0):
     """One decode step, state [B, H, Dk, Dv] fp32 updated in place (include/kda.h).
+    frontend: KDA_FRONT_* bits applied to raw inputs (kda_decode_step_ex).
     Returns o [B, H, Dv] fp32."""
     dev = q.device
     Bsz, H, Dk = q.shape
@@ -126,8 +132,12 @@ def kda_decode_step(q, k, v, g, beta, state, o=None):
     if o is None:
         o = torch.empty((Bsz, H, Dv), dtype=torch.float32, device=dev)
     _check(o, "o", torch.float32, (Bsz, H, Dv), dev)
-    st = B.decode_raw(_ptr(q), _ptr(k), _ptr(v), code, _ptr(g), _ptr(beta), Bsz, H, Dk, Dv,
-                      _ptr(state), _ptr(o), _stream(dev))
+    if frontend:
+        st = B.decode_ex_raw(_ptr(q), _ptr(k), _ptr(v), code, _ptr(g), _ptr(beta), Bsz, H, Dk,
+                             Dv, _ptr(state), _ptr(o), int(frontend), _stream(dev))
+    else:
+        st = B.decode_raw(_ptr(q), _ptr(k), _ptr(v), code, _ptr(g), _ptr(beta), Bsz, H, Dk, Dv,
+                          _ptr(state), _ptr(o), _stream(dev))
     if st != B.KDA_OK:
         raise B.KdaError(st, "kda_decode_step")
     return o

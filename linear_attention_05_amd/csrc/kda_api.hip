@@ -7,13 +7,18 @@
 
 namespace {
 
-constexpr int kVersion = 100;  // 0.1.0
+constexpr int kVersion = 200;  // 0.2.0
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 bool supported_dim(int32_t d) { return d == 64 || d == 128; }
 
 bool valid_dtype(kda_dtype_t t) { return t == KDA_F32 || t == KDA_BF16; }
+
+constexpr uint32_t kFrontMask = KDA_FRONT_L2NORM_QK | KDA_FRONT_GATE | KDA_FRONT_BETA_SIGMOID;
+static_assert(KDA_FRONT_L2NORM_QK == kda::kFrontL2 && KDA_FRONT_GATE == kda::kFrontGate &&
+                  KDA_FRONT_BETA_SIGMOID == kda::kFrontBeta,
+              "front-end bits of kda.h and the kernels differ");
 
 // Shared size checks of the prefill entry points (sizes only, no pointers).
 kda_status_t check_prefill_sizes(int64_t total_tokens, int32_t num_seqs, int32_t H, int32_t Dk,
@@ -51,17 +56,18 @@ size_t kda_prefill_workspace_size(int64_t total_tokens, int32_t num_seqs, int32_
     return kda::prefill_workspace_bytes(total_tokens, num_seqs, H, Dk, Dv, in_dtype == KDA_BF16);
 }
 
-kda_status_t kda_prefill_chunked_phases(const void* q, const void* k, const void* v,
-                                        kda_dtype_t in_dtype, const float* g, const float* beta,
-                                        const int32_t* cu_seqlens, int32_t num_seqs,
-                                        int64_t total_tokens, int32_t H, int32_t Dk, int32_t Dv,
-                                        int32_t chunk_size, const float* initial_state,
-                                        float* final_state, int64_t ckpt_interval,
-                                        float* ckpt_states, int64_t ckpt_rows, float* o,
-                                        void* workspace, size_t workspace_bytes, uint32_t phases,
-                                        hipStream_t stream) {
+kda_status_t kda_prefill_chunked_ex(const void* q, const void* k, const void* v,
+                                    kda_dtype_t in_dtype, const float* g, const float* beta,
+                                    const int32_t* cu_seqlens, int32_t num_seqs,
+                                    int64_t total_tokens, int32_t H, int32_t Dk, int32_t Dv,
+                                    int32_t chunk_size, const float* initial_state,
+                                    float* final_state, int64_t ckpt_interval,
+                                    float* ckpt_states, int64_t ckpt_rows, float* o,
+                                    void* workspace, size_t workspace_bytes, uint32_t phases,
+                                    uint32_t frontend, hipStream_t stream) {
     if (phases == 0 || (phases & ~(KDA_PHASE_PREPARE | KDA_PHASE_SCAN)) != 0)
         return KDA_ERR_INVALID_ARG;
+    if (frontend & ~kFrontMask) return KDA_ERR_INVALID_ARG;
     kda_status_t st = check_prefill_sizes(total_tokens, num_seqs, H, Dk, Dv, chunk_size, in_dtype);
     if (st != KDA_OK) return st;
     if (!cu_seqlens && num_seqs != 1) return KDA_ERR_INVALID_ARG;
@@ -100,7 +106,23 @@ kda_status_t kda_prefill_chunked_phases(const void* q, const void* k, const void
     a.workspace = workspace;
     a.workspace_bytes = workspace_bytes;
     a.phases = phases;
+    a.frontend = frontend;
     return kda::launch_prefill(a, stream) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status_t kda_prefill_chunked_phases(const void* q, const void* k, const void* v,
+                                        kda_dtype_t in_dtype, const float* g, const float* beta,
+                                        const int32_t* cu_seqlens, int32_t num_seqs,
+                                        int64_t total_tokens, int32_t H, int32_t Dk, int32_t Dv,
+                                        int32_t chunk_size, const float* initial_state,
+                                        float* final_state, int64_t ckpt_interval,
+                                        float* ckpt_states, int64_t ckpt_rows, float* o,
+                                        void* workspace, size_t workspace_bytes, uint32_t phases,
+                                        hipStream_t stream) {
+    return kda_prefill_chunked_ex(q, k, v, in_dtype, g, beta, cu_seqlens, num_seqs, total_tokens,
+                                  H, Dk, Dv, chunk_size, initial_state, final_state,
+                                  ckpt_interval, ckpt_states, ckpt_rows, o, workspace,
+                                  workspace_bytes, phases, 0u, stream);
 }
 
 kda_status_t kda_prefill_chunked(const void* q, const void* k, const void* v,
@@ -118,9 +140,11 @@ kda_status_t kda_prefill_chunked(const void* q, const void* k, const void* v,
                                       KDA_PHASE_PREPARE | KDA_PHASE_SCAN, stream);
 }
 
-kda_status_t kda_decode_step(const void* q, const void* k, const void* v, kda_dtype_t in_dtype,
-                             const float* g, const float* beta, int32_t B, int32_t H, int32_t Dk,
-                             int32_t Dv, float* state, float* o, hipStream_t stream) {
+kda_status_t kda_decode_step_ex(const void* q, const void* k, const void* v,
+                                kda_dtype_t in_dtype, const float* g, const float* beta,
+                                int32_t B, int32_t H, int32_t Dk, int32_t Dv, float* state,
+                                float* o, uint32_t frontend, hipStream_t stream) {
+    if (frontend & ~kFrontMask) return KDA_ERR_INVALID_ARG;
     if (B < 0 || H < 1 || Dk < 1 || Dv < 1 || !valid_dtype(in_dtype)) return KDA_ERR_INVALID_ARG;
     if (!supported_dim(Dk) || !supported_dim(Dv)) return KDA_ERR_UNSUPPORTED;
     if ((int64_t)B * H > (int64_t)INT32_MAX) return KDA_ERR_UNSUPPORTED;
@@ -130,9 +154,15 @@ kda_status_t kda_decode_step(const void* q, const void* k, const void* v, kda_dt
     for (const void* p : ptrs)
         if (!aligned(p, 16)) return KDA_ERR_INVALID_ARG;
     return kda::launch_decode(q, k, v, in_dtype == KDA_BF16, g, beta, B, H, Dk, Dv, state, o,
-                              stream) == hipSuccess
+                              frontend, stream) == hipSuccess
                ? KDA_OK
                : KDA_ERR_HIP;
+}
+
+kda_status_t kda_decode_step(const void* q, const void* k, const void* v, kda_dtype_t in_dtype,
+                             const float* g, const float* beta, int32_t B, int32_t H, int32_t Dk,
+                             int32_t Dv, float* state, float* o, hipStream_t stream) {
+    return kda_decode_step_ex(q, k, v, in_dtype, g, beta, B, H, Dk, Dv, state, o, 0u, stream);
 }
 
 }  // extern "C"

@@ -25,7 +25,16 @@
 // workgroups 5.4-5.55 at any residency. The launch therefore asks for enough
 // (unused) dynamic LDS that only n workgroups fit on a CU, n = 64 KiB / state
 // bytes (at least 1), keeping about 64 KiB of state in flight per CU.
+//
+// Optional parameter-free front-end (KDA's query/key L2 normalisation and
+// gate activations; Kimi K3 report, "Methodology notes", Kimi Delta
+// Attention): with L2, k and q are scaled by 1/sqrt(sum x^2 + 1e-6) in fp32
+// (every wave loads both rows and reduces their norms itself while the state
+// is in flight; the butterfly gives every lane the same bits); `front` bit kFrontGate reads g as u and uses -exp(u), bit
+// kFrontBeta reads beta as a logit and uses its sigmoid.
 #include "kda_internal.h"
+
+#include <type_traits>
 
 namespace kda {
 namespace {
@@ -45,6 +54,22 @@ __device__ __forceinline__ float load_in(const void* p, int64_t i) {
         return static_cast<const float*>(p)[i];
 }
 
+// Raw input element (bf16 bits or fp32), converted later by in_f32: keeps the
+// wait for the load out of the code that issues the next loads.
+template <bool BF16>
+using raw_t = typename std::conditional<BF16, unsigned short, float>::type;
+
+template <bool BF16>
+__device__ __forceinline__ raw_t<BF16> load_raw(const void* p, int64_t i) {
+    return static_cast<const raw_t<BF16>*>(p)[i];
+}
+
+template <bool BF16>
+__device__ __forceinline__ float in_f32(raw_t<BF16> x) {
+    if constexpr (BF16) return bf16_to_f32(x);
+    else return x;
+}
+
 template <bool BF16>
 __device__ __forceinline__ f32x4 load_in4(const void* p, int64_t i) {
     if constexpr (BF16) {
@@ -58,18 +83,21 @@ __device__ __forceinline__ f32x4 load_in4(const void* p, int64_t i) {
 constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
 
-template <int DK, int DV, bool BF16>
+template <int DK, int DV, bool BF16, bool L2>
 __global__ __launch_bounds__(kThreads) void decode_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, float* __restrict__ state,
-    float* __restrict__ o) {
+    float* __restrict__ o, unsigned front) {
     constexpr int CG = DV / 4;           // column groups (threads per row)
     constexpr int RG = kThreads / CG;    // row groups
     constexpr int RPT = DK / RG;         // rows per thread
     constexpr int RGW = 64 / CG;         // row groups per wave
     static_assert(RPT * RG == DK && CG * 4 == DV && RGW >= 1, "bad decode tiling");
 
-    __shared__ float s_a[DK], s_k[DK], s_q[DK];
+    // per-row vectors, one slot per thread: every thread stores its slot (rows
+    // past DK are never read), so no branch invites the compiler to sink the
+    // row loads behind the state loads
+    __shared__ float s_a[kThreads], s_k[kThreads], s_q[kThreads];
     __shared__ f32x4 s_red[kWaves][CG][2];
     __shared__ float s_kq[kWaves];
 
@@ -81,21 +109,57 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
     const int64_t pair = blockIdx.x;  // b * H + h
     float* S = state + pair * (int64_t)(DK * DV);
 
-    // 1. stream the thread's state slab in (all loads in flight at once)
+    // 1. the small per-(b, h) inputs first: the memory counter completes in
+    // issue order, so waiting for them does not wait for the state
+    static_assert(DK <= kThreads, "one key row per thread");
+    const int tr = t < DK ? t : DK - 1;  // unconditional loads (no branch to join)
+    float graw = g[pair * DK + tr];
+    const raw_t<BF16> kraw = load_raw<BF16>(k, pair * DK + tr);
+    const raw_t<BF16> qraw = load_raw<BF16>(q, pair * DK + tr);
+    const f32x4 vv = load_in4<BF16>(v, pair * DV + 4 * cg);
+    float bt = beta[pair];
+    raw_t<BF16> kw[L2 ? DK / 64 : 1], qw[L2 ? DK / 64 : 1];  // whole k and q rows for the norms
+    if constexpr (L2) {
+#pragma unroll
+        for (int j = 0; j < DK / 64; ++j) {
+            kw[j] = load_raw<BF16>(k, pair * DK + lane + 64 * j);
+            qw[j] = load_raw<BF16>(q, pair * DK + lane + 64 * j);
+        }
+    }
+    asm volatile("" ::: "memory");  // keep them ahead of the state loads
+    __builtin_amdgcn_sched_barrier(0);
+
+    // 2. stream the thread's state slab in (all loads in flight at once)
     f32x4 s[RPT];
 #pragma unroll
     for (int m = 0; m < RPT; ++m)
         s[m] = __builtin_nontemporal_load(
             reinterpret_cast<const f32x4*>(S + (int64_t)(rg + m * RG) * DV) + cg);
+    __builtin_amdgcn_sched_barrier(0);
 
-    // 2. per-row vectors into LDS; per-column inputs straight to registers
-    for (int i = t; i < DK; i += kThreads) {
-        s_a[i] = __expf(g[pair * DK + i]);
-        s_k[i] = load_in<BF16>(k, pair * DK + i);
-        s_q[i] = load_in<BF16>(q, pair * DK + i);
+    // while the state is in flight: activations, norms, per-row vectors to LDS
+    if (front & kFrontGate) graw = -__expf(graw);
+    s_a[t] = __expf(graw);
+    s_k[t] = in_f32<BF16>(kraw);
+    s_q[t] = in_f32<BF16>(qraw);
+    if (front & kFrontBeta) bt = 1.f / (1.f + __expf(-bt));
+    float kn = 1.f, qn = 1.f;  // inverse norms of k and q (L2)
+    if constexpr (L2) {
+        float sk = 0.f, sq = 0.f;
+#pragma unroll
+        for (int j = 0; j < DK / 64; ++j) {
+            const float kx = in_f32<BF16>(kw[j]), qx = in_f32<BF16>(qw[j]);
+            sk += kx * kx;
+            sq += qx * qx;
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+            sk += __shfl_xor(sk, off);
+            sq += __shfl_xor(sq, off);
+        }
+        kn = 1.f / sqrtf(sk + kL2Eps);
+        qn = 1.f / sqrtf(sq + kL2Eps);
     }
-    const f32x4 vv = load_in4<BF16>(v, pair * DV + 4 * cg);
-    const float bt = beta[pair];
     __syncthreads();
 
     // 3. decay in registers; partial S'^T k, S'^T q and k.q over this thread's rows
@@ -104,7 +168,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
 #pragma unroll
     for (int m = 0; m < RPT; ++m) {
         const int i = rg + m * RG;
-        const float ai = s_a[i], ki = s_k[i], qi = s_q[i];
+        const float ai = s_a[i], ki = s_k[i] * kn, qi = s_q[i] * qn;
         s[m] *= ai;
         r += s[m] * ki;
         p += s[m] * qi;
@@ -148,7 +212,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
 #pragma unroll
     for (int m = 0; m < RPT; ++m) {
         const int i = rg + m * RG;
-        const f32x4 nv = s[m] + s_k[i] * u;
+        const f32x4 nv = s[m] + (s_k[i] * kn) * u;
         __builtin_nontemporal_store(nv, reinterpret_cast<f32x4*>(S + (int64_t)i * DV) + cg);
     }
 }
@@ -160,7 +224,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
 template <int DK, int DV>
 unsigned residency_pad() {
     constexpr int CG = DV / 4;
-    constexpr int kStatic = 3 * DK * 4 + kWaves * CG * 2 * 16 + kWaves * 4;
+    constexpr int kStatic = 3 * kThreads * 4 + kWaves * CG * 2 * 16 + kWaves * 4;
     const int n = (DK * DV * 4 >= 65536) ? 1 : 65536 / (DK * DV * 4);
     int lds = 0, dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 0;
@@ -176,16 +240,14 @@ unsigned residency_pad() {
 
 template <int DK, int DV>
 hipError_t launch_dims(const void* q, const void* k, const void* v, bool bf16, const float* g,
-                       const float* beta, int B, int H, float* state, float* o,
+                       const float* beta, int B, int H, float* state, float* o, unsigned front,
                        hipStream_t stream) {
     const dim3 grid((unsigned)((int64_t)B * H)), block(kThreads);
     const unsigned pad = residency_pad<DK, DV>();
-    if (bf16)
-        hipLaunchKernelGGL((decode_kernel<DK, DV, true>), grid, block, pad, stream, q, k, v, g,
-                           beta, state, o);
-    else
-        hipLaunchKernelGGL((decode_kernel<DK, DV, false>), grid, block, pad, stream, q, k, v, g,
-                           beta, state, o);
+    const bool l2 = (front & kFrontL2) != 0;
+    auto kern = bf16 ? (l2 ? &decode_kernel<DK, DV, true, true> : &decode_kernel<DK, DV, true, false>)
+                     : (l2 ? &decode_kernel<DK, DV, false, true> : &decode_kernel<DK, DV, false, false>);
+    hipLaunchKernelGGL(kern, grid, block, pad, stream, q, k, v, g, beta, state, o, front);
     return hipGetLastError();
 }
 
@@ -193,12 +255,12 @@ hipError_t launch_dims(const void* q, const void* k, const void* v, bool bf16, c
 
 hipError_t launch_decode(const void* q, const void* k, const void* v, bool bf16,
                          const float* g, const float* beta, int B, int H, int Dk, int Dv,
-                         float* state, float* o, hipStream_t stream) {
+                         float* state, float* o, unsigned front, hipStream_t stream) {
     if ((int64_t)B * H == 0) return hipSuccess;
-    if (Dk == 128 && Dv == 128) return launch_dims<128, 128>(q, k, v, bf16, g, beta, B, H, state, o, stream);
-    if (Dk == 128 && Dv == 64) return launch_dims<128, 64>(q, k, v, bf16, g, beta, B, H, state, o, stream);
-    if (Dk == 64 && Dv == 128) return launch_dims<64, 128>(q, k, v, bf16, g, beta, B, H, state, o, stream);
-    if (Dk == 64 && Dv == 64) return launch_dims<64, 64>(q, k, v, bf16, g, beta, B, H, state, o, stream);
+    if (Dk == 128 && Dv == 128) return launch_dims<128, 128>(q, k, v, bf16, g, beta, B, H, state, o, front, stream);
+    if (Dk == 128 && Dv == 64) return launch_dims<128, 64>(q, k, v, bf16, g, beta, B, H, state, o, front, stream);
+    if (Dk == 64 && Dv == 128) return launch_dims<64, 128>(q, k, v, bf16, g, beta, B, H, state, o, front, stream);
+    if (Dk == 64 && Dv == 64) return launch_dims<64, 64>(q, k, v, bf16, g, beta, B, H, state, o, front, stream);
     return hipErrorInvalidValue;
 }
 

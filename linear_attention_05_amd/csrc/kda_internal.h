@@ -8,10 +8,17 @@
 
 namespace kda {
 
+// Parameter-free front-end applied inside the kernels (KDA_FRONT_* of kda.h):
+// q/k L2 normalisation with this epsilon inside the root, g read as u with
+// log-decay -exp(u), beta read as a logit.
+constexpr unsigned kFrontL2 = 1u, kFrontGate = 2u, kFrontBeta = 4u;
+constexpr unsigned kFrontAll = kFrontL2 | kFrontGate | kFrontBeta;
+constexpr float kL2Eps = 1e-6f;
+
 // ---- decode ---------------------------------------------------------------
 hipError_t launch_decode(const void* q, const void* k, const void* v, bool bf16,
                          const float* g, const float* beta, int B, int H, int Dk, int Dv,
-                         float* state, float* o, hipStream_t stream);
+                         float* state, float* o, unsigned frontend, hipStream_t stream);
 
 // ---- prefill --------------------------------------------------------------
 struct PrefillArgs {
@@ -33,7 +40,8 @@ struct PrefillArgs {
     float* o;
     void* workspace;
     size_t workspace_bytes;
-    unsigned phases;  // bit 0: prepare (prep + K1), bit 1: scan (K2)
+    unsigned phases;    // bit 0: prepare (prep + K1), bit 1: scan (K2)
+    unsigned frontend;  // kFront* bits (0: inputs used as given)
 };
 
 // Bytes of workspace the prefill path needs (0 if unsupported).

@@ -60,6 +60,13 @@ __device__ __forceinline__ float bf16_to_f32(unsigned short b) {
     return __uint_as_float(static_cast<unsigned>(b) << 16);
 }
 
+// An input element (bf16 bits or fp32) as fp32.
+template <typename T>
+__device__ __forceinline__ float qf_in(T v) {
+    if constexpr (std::is_same<T, float>::value) return v;
+    else return bf16_to_f32(v);
+}
+
 // Sum of a value over lane pairs (l, l ^ 16) / (l, l ^ 32), with the two
 // addends in the same order in both lanes (v_permlane16/32_swap).
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
@@ -266,12 +273,22 @@ __device__ __forceinline__ void locate_chunk(int ci, const int32_t* cu, const in
 //           columns 16w..16w+15, four lanes share a column and split each
 //           row's inner sum, two lane exchanges combine them
 //   W       -W = -Ainv diag(beta) Kd via MFMA on W^T tiles; Ab = Ainv diag(beta)
-template <int DK, bool BF16>
+//
+// Optional parameter-free front-end (KDA's query/key L2 normalisation and
+// gate activations; Kimi K3 report, "Methodology notes", Kimi Delta
+// Attention): with L2 every key and query row is scaled by
+// 1/sqrt(sum x^2 + 1e-6) in fp32. Key rows are rewritten normalised in LDS
+// (bf16 input: as fp16 in the same 16-bit slots, so the normalised key is
+// rounded once to fp16 before its MFMA operand is formed; fp32 input: fp32);
+// query rows are scaled where they enter an operand. `front` bit kFrontGate
+// reads g as u and uses -exp(u), bit kFrontBeta reads beta as a logit and
+// uses its sigmoid.
+template <int DK, bool BF16, bool L2>
 __global__ __launch_bounds__(kThreads, BF16 ? 3 : 2) void k1_prep_kernel(
     const void* __restrict__ qin, const void* __restrict__ kin, const float* __restrict__ g,
     const float* __restrict__ beta, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ chunk_start, int num_seqs, int64_t N, int H, int64_t max_chunks,
-    unsigned char* __restrict__ handoff) {
+    unsigned front, unsigned char* __restrict__ handoff) {
     using M = Mma<BF16>;
     using E = typename M::E;
     using Frag = typename M::Frag;
@@ -295,6 +312,7 @@ __global__ __launch_bounds__(kThreads, BF16 ? 3 : 2) void k1_prep_kernel(
     __shared__ __attribute__((aligned(16))) float sG[C][GP];  // g, then G * log2(e)
     __shared__ float sB[C];
     __shared__ double sTot[NQ][DK];
+    __shared__ float sQn[L2 ? C : 1];  // inverse query-row norms
     TIn(*sK)[KP] = reinterpret_cast<TIn(*)[KP]>(sKA);
     float(*sA)[AP] = reinterpret_cast<float(*)[AP]>(sKA);
 
@@ -370,9 +388,34 @@ __global__ __launch_bounds__(kThreads, BF16 ? 3 : 2) void k1_prep_kernel(
     for (int u = 0; u < GV; ++u) {
         const int i = t + u * kThreads;
         const int r = i / (DK / 4), c = (i % (DK / 4)) * 4;
-        *reinterpret_cast<f32x4*>(&sG[r][c]) = greg[u];
+        f32x4 gv = greg[u];
+        if ((front & kFrontGate) && r < len) {  // g = -exp(u); rows past the end stay 0
+#pragma unroll
+            for (int e = 0; e < 4; ++e) gv[e] = -__expf(gv[e]);
+        }
+        *reinterpret_cast<f32x4*>(&sG[r][c]) = gv;
     }
-    if (t < C) sB[t] = breg;
+    if (t < C) sB[t] = ((front & kFrontBeta) && t < len) ? 1.f / (1.f + __expf(-breg)) : breg;
+    // inverse query-row norms from this wave's phase-A rows: the four lanes
+    // m + 16q hold the channels of row 16 rb + m between them
+    if constexpr (L2) {
+#pragma unroll
+        for (int gi = 0; gi < 2; ++gi) {
+            const int rb = plan[wave][gi][0];
+            if (rb < 0) break;
+            float ss = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float x = qf_in<TIn>(qa[gi][ks][e]);
+                    ss += x * x;
+                }
+            ss += __shfl_xor(ss, 16);
+            ss += __shfl_xor(ss, 32);
+            if (q == 0) sQn[16 * rb + m] = 1.f / sqrtf(ss + kL2Eps);  // rows shared by two waves get equal values
+        }
+    }
     __syncthreads();
     {
         // inclusive cumulative sum per channel in fp64 (rows past the end add 0)
@@ -381,6 +424,35 @@ __global__ __launch_bounds__(kThreads, BF16 ? 3 : 2) void k1_prep_kernel(
 #pragma unroll
         for (int r = grp * RPQ; r < (grp + 1) * RPQ; ++r) acc += (double)sG[r][c];
         sTot[grp][c] = acc;
+        if constexpr (L2) {  // key rows normalised in place: four threads per row
+            constexpr int NV = DK / 4 / VEC;  // 16-byte vectors per thread
+            const int r = t >> 2, part = t & 3;
+            vecK_t* row = reinterpret_cast<vecK_t*>(&sK[r][part * (DK / 4)]);
+            vecK_t kv[NV];
+            float ss = 0.f;
+#pragma unroll
+            for (int j = 0; j < NV; ++j) {
+                kv[j] = row[j];
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) {
+                    const float x = qf_in<TIn>(kv[j][e]);
+                    ss += x * x;
+                }
+            }
+            ss += __shfl_xor(ss, 1);
+            ss += __shfl_xor(ss, 2);
+            const float inv = 1.f / sqrtf(ss + kL2Eps);
+#pragma unroll
+            for (int j = 0; j < NV; ++j) {
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) {
+                    const float x = qf_in<TIn>(kv[j][e]) * inv;
+                    if constexpr (BF16) kv[j][e] = __builtin_bit_cast(unsigned short, (_Float16)x);
+                    else kv[j][e] = x;
+                }
+                row[j] = kv[j];
+            }
+        }
         __syncthreads();
         double run = 0.0;
         for (int p = 0; p < grp; ++p) run += sTot[p][c];
@@ -392,9 +464,9 @@ __global__ __launch_bounds__(kThreads, BF16 ? 3 : 2) void k1_prep_kernel(
     }
     __syncthreads();
 
-    auto kval = [&](int r, int c) -> float {
-        if constexpr (BF16) return bf16_to_f32(sK[r][c]);
-        else return sK[r][c];
+    auto kval = [&](int r, int c) -> float {  // key value (normalised fp16 bits: L2 and bf16)
+        if constexpr (L2 && BF16) return (float)__builtin_bit_cast(_Float16, sK[r][c]);
+        else return qf_in<TIn>(sK[r][c]);
     };
     auto qf = [&](TIn v) -> float {
         if constexpr (BF16) return bf16_to_f32(v);
@@ -427,6 +499,7 @@ __global__ __launch_bounds__(kThreads, BF16 ? 3 : 2) void k1_prep_kernel(
             if (rb < 0) break;
             const int ref = 16 * rb;
             const int r = 16 * rb + m;
+            const float zq = L2 ? sQn[r] : 1.f;
             Frag X[NKS], Z[NKS];
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
@@ -435,7 +508,7 @@ __global__ __launch_bounds__(kThreads, BF16 ? 3 : 2) void k1_prep_kernel(
                     const int c = 32 * ks + 8 * q + e;
                     const float fr = fast_exp2(sG[r][c] - sG[ref][c]);
                     X[ks][e] = (E)(kval(r, c) * fr);
-                    Z[ks][e] = (E)(qf(qa[gi][ks][e]) * fr);
+                    Z[ks][e] = (E)(qf(qa[gi][ks][e]) * zq * fr);
                 }
             }
 #pragma unroll
@@ -497,7 +570,7 @@ __global__ __launch_bounds__(kThreads, BF16 ? 3 : 2) void k1_prep_kernel(
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int c = 32 * ks + perm32(q, e);
-                out[e] = (E)(qf(qd[i][e >> 2][e & 3]) * fast_exp2(sG[r][c]));
+                out[e] = (E)(qf(qd[i][e >> 2][e & 3]) * (L2 ? sQn[r] : 1.f) * fast_exp2(sG[r][c]));
             }
             store_frag<Frag, E>(hb + HO::kQd, rt * NKS + ks, lane, out);
         }
@@ -1835,11 +1908,13 @@ hipError_t launch_typed(const PrefillArgs& a, hipStream_t stream) {
     if (prepare && varlen)
         hipLaunchKernelGGL(prep_kernel, dim3(1), dim3(kThreads), 0, stream, a.cu_seqlens, a.num_seqs,
                            a.total_tokens, a.ckpt_interval, p.chunk_start, p.ckpt_base, p.order);
-    if (prepare && p.max_chunks > 0 && a.total_tokens > 0)
-        hipLaunchKernelGGL((k1_prep_kernel<DK, BF16>), dim3((unsigned)(p.max_chunks * a.H)),
-                           dim3(kThreads), 0, stream, a.q, a.k, a.g, a.beta, a.cu_seqlens,
-                           varlen ? p.chunk_start : nullptr, a.num_seqs, a.total_tokens, a.H,
-                           p.max_chunks, p.handoff);
+    if (prepare && p.max_chunks > 0 && a.total_tokens > 0) {
+        auto k1 = (a.frontend & kFrontL2) ? &k1_prep_kernel<DK, BF16, true>
+                                          : &k1_prep_kernel<DK, BF16, false>;
+        hipLaunchKernelGGL(k1, dim3((unsigned)(p.max_chunks * a.H)), dim3(kThreads), 0, stream,
+                           a.q, a.k, a.g, a.beta, a.cu_seqlens, varlen ? p.chunk_start : nullptr,
+                           a.num_seqs, a.total_tokens, a.H, p.max_chunks, a.frontend, p.handoff);
+    }
     // Scan design. Every scan workgroup streams the whole handoff of its
     // (sequence, head) through its CU, about 63 KB per chunk for D = 128, and
     // a CU's vector-memory path (~50 B/clk from L2) bounds each chunk step.

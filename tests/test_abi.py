@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert B.version() >= 100
+    assert B.version() >= 200  # 0.2.0: the *_ex entry points
     for s in range(5):
         assert B.status_string(s).startswith("KDA_")
     assert "unknown" in B.status_string(99)
@@ -90,6 +90,32 @@ def test_prefill_validation(kw, status):
 def test_prefill_phases_validation(phases, status):
     st = B.prefill_phases_raw(A, A, A, B.KDA_BF16, A, A, None, 1, 256, 2, 128, 128, 64, None, A,
                               0, None, 0, A, A, 10 ** 12, phases, None)
+    assert st == status
+
+
+@pytest.mark.parametrize("front,kw,status", [
+    (8, {}, INV), (0xFFFFFFFF, {}, INV),               # unknown front-end bits
+    (B.FRONT_ALL, dict(q=None), INV), (B.FRONT_ALL, dict(Dk=96), UNS),
+    (B.FRONT_ALL, dict(wsb=1000), WS), (B.FRONT_GATE, dict(phases=0), INV),
+])
+def test_prefill_ex_validation(front, kw, status):
+    a = dict(q=A, Dk=128, wsb=10 ** 12, phases=3)
+    a.update(kw)
+    st = B.prefill_ex_raw(a["q"], A, A, B.KDA_BF16, A, A, None, 1, 256, 2, a["Dk"], 128, 64,
+                          None, A, 0, None, 0, A, A, a["wsb"], a["phases"], front, None)
+    assert st == status
+
+
+@pytest.mark.parametrize("front,kw,status", [
+    (8, {}, INV), (16, dict(B=0), INV),                # unknown bits, even for a no-op
+    (B.FRONT_ALL, dict(B=0), OK), (B.FRONT_L2NORM_QK, dict(Dk=32), UNS),
+    (B.FRONT_BETA_SIGMOID, dict(st=None), INV),
+])
+def test_decode_ex_validation(front, kw, status):
+    a = dict(B=4, Dk=128, st=A)
+    a.update(kw)
+    st = B.decode_ex_raw(A, A, A, B.KDA_BF16, A, A, a["B"], 2, a["Dk"], 128, a["st"], A, front,
+                         None)
     assert st == status
 
 
