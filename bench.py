@@ -324,6 +324,53 @@ def bench_frontend(steps=10, warmup=3, decode_steps=32):
         decode_plain_us_per_step=round(dec_plain * 1e3, 2))
 
 
+def bench_positions(reps=10, warmup=3):
+    """States at arbitrary positions (kda_prefill_chunked_at) on the headline
+    prefill: whole calls with four mid-chunk positions, interleaved with plain
+    calls on the same inputs."""
+    import numpy as np
+    import torch
+    import linear_attention_05_amd as K
+    from synth import make_workload
+
+    x = make_workload(PREFILL_WORKLOAD)
+    N, H, D = x.total_tokens, x.H, x.Dk
+    args = [dev(a) for a in (x.q, x.k, x.v, x.g, x.beta)]
+    s0 = dev(x.initial_state)
+    o = torch.empty(N, H, D, device="cuda")
+    fs = torch.empty(1, H, D, D, device="cuda")
+    ws = torch.empty(K.kda_prefill_workspace_size(N, 1, H, D, D), dtype=torch.uint8, device="cuda")
+    vals = [1000, 3000, 5000, N - 1]
+    offs = torch.tensor([0, len(vals)], dtype=torch.int32, device="cuda")
+    pv = torch.tensor(vals, dtype=torch.int32, device="cuda")
+    ps = torch.empty(len(vals), H, D, D, device="cuda")
+
+    def plain():
+        K.kda_prefill_chunked(*args, initial_state=s0, final_state=fs, o=o, workspace=ws)
+
+    def at():
+        K.kda_prefill_chunked_at(*args, offs, pv, pos_states=ps, initial_state=s0,
+                                 final_state=fs, o=o, workspace=ws)
+
+    for _ in range(warmup):
+        plain()
+        at()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
+    torch.cuda.synchronize()
+    for e in ev:
+        e[0].record()
+        plain()
+        e[1].record()
+        at()
+        e[2].record()
+    torch.cuda.synchronize()
+    t_plain = float(np.median([e[0].elapsed_time(e[1]) for e in ev]))
+    t_at = float(np.median([e[1].elapsed_time(e[2]) for e in ev]))
+    return dict(workload=f"prefill B=1 T={N} H={H} D={D} bf16, states after {vals} tokens",
+                plain_ms=round(t_plain, 4), with_positions_ms=round(t_at, 4),
+                overhead_ms=round(t_at - t_plain, 4))
+
+
 def hbm_ceilings():
     """Practical HBM rates of plain torch kernels on 1 GiB (context for the
     roofline fractions): read-only (sum), write-only (fill), copy (read+write)."""
@@ -455,6 +502,7 @@ def main():
         out["prefill_workloads"] = [bench_prefill_workload(2), bench_prefill_workload(3)]
     if args.only == "all" and not args.no_extra_workloads:
         out["frontend"] = bench_frontend()
+        out["positions"] = bench_positions()
         out["hbm_ceilings"] = hbm_ceilings()
     if args.only in ("all", "prefill") and not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(p["inputs"])

@@ -188,10 +188,10 @@ kda_status_t kda_prefill_chunked_phases(
 /*
  * kda_prefill_chunked_phases with a `frontend` mask (a subset of the
  * KDA_FRONT_* bits; 0 = kda_prefill_chunked_phases). The transforms act in
- * the PREPARE phase, the only one that reads q, k, g and beta; a SCAN-only
- * call ignores them. The documented decay precondition then applies to
- * -exp(u). Returns KDA_ERR_INVALID_ARG for unknown bits, otherwise as
- * kda_prefill_chunked_phases.
+ * the PREPARE phase, the only one that reads q, k, g and beta here; a
+ * SCAN-only call ignores them. The documented decay precondition then
+ * applies to -exp(u). Returns KDA_ERR_INVALID_ARG for unknown bits,
+ * otherwise as kda_prefill_chunked_phases.
  */
 kda_status_t kda_prefill_chunked_ex(
     const void *q, const void *k, const void *v, kda_dtype_t in_dtype,
@@ -201,6 +201,43 @@ kda_status_t kda_prefill_chunked_ex(
     int64_t ckpt_interval, float *ckpt_states, int64_t ckpt_rows, float *o,
     void *workspace, size_t workspace_bytes, uint32_t phases, uint32_t frontend,
     hipStream_t stream);
+
+/*
+ * kda_prefill_chunked_ex that also returns states at arbitrary positions,
+ * for example prompt boundaries whose state a serving system caches
+ * (the Kimi K3 report's deployment notes mention caching the recurrent
+ * state at prompt boundaries).
+ *
+ *   pos_offsets  device int32 [num_seqs + 1]: the positions of sequence s
+ *                are pos_values[pos_offsets[s] .. pos_offsets[s + 1])
+ *                (non-decreasing offsets; pos_offsets[num_seqs] = num_pos)
+ *   pos_values   device int32 [num_pos]: token counts P, 0 <= P <= L_s,
+ *                non-decreasing within a sequence (P = 0 is the initial
+ *                state, P = L_s the final state)
+ *   num_pos      number of positions (>= 0); 0 = kda_prefill_chunked_ex and
+ *                the three position arguments are ignored
+ *   pos_states   [num_pos, H, Dk, Dv] fp32: slot j receives the state after
+ *                the first pos_values[j] tokens of its sequence
+ *
+ * The scan stores the state at the start of the chunk that holds each P and
+ * a small kernel runs the remaining P mod 64 tokens of the recurrence on it
+ * in fp32; both belong to the SCAN phase, which then also reads k, v, g and
+ * beta, so a split call must pass the same `frontend` bits to both phases.
+ * Device-side (unchecked) preconditions: P outside [0, L_s] is clamped into
+ * it; offsets outside [0, num_pos] are clamped; out-of-order positions give
+ * unspecified states in their slots (never an out-of-bounds access).
+ * Returns KDA_ERR_INVALID_ARG for num_pos < 0, or num_pos > 0 with a NULL or
+ * misaligned position argument; otherwise as kda_prefill_chunked_ex.
+ */
+kda_status_t kda_prefill_chunked_at(
+    const void *q, const void *k, const void *v, kda_dtype_t in_dtype,
+    const float *g, const float *beta, const int32_t *cu_seqlens,
+    int32_t num_seqs, int64_t total_tokens, int32_t H, int32_t Dk, int32_t Dv,
+    int32_t chunk_size, const float *initial_state, float *final_state,
+    int64_t ckpt_interval, float *ckpt_states, int64_t ckpt_rows, float *o,
+    const int32_t *pos_offsets, const int32_t *pos_values, int32_t num_pos,
+    float *pos_states, void *workspace, size_t workspace_bytes, uint32_t phases,
+    uint32_t frontend, hipStream_t stream);
 
 /*
  * One KDA decode step for B independent sequences (one new token each).

@@ -19,6 +19,7 @@ KDA_F32, KDA_BF16 = 0, 1
 # Every symbol include/kda.h declares.
 EXPORTS = ("kda_version", "kda_status_string", "kda_prefill_workspace_size",
            "kda_prefill_chunked", "kda_prefill_chunked_phases", "kda_prefill_chunked_ex",
+           "kda_prefill_chunked_at",
            "kda_decode_step", "kda_decode_step_ex")
 PHASE_PREPARE, PHASE_SCAN = 1, 2
 # KDA_FRONT_* bits of include/kda.h
@@ -61,6 +62,9 @@ def load():
     lib.kda_prefill_chunked_ex.argtypes = list(lib.kda_prefill_chunked.argtypes[:-1]) + [
         ctypes.c_uint32, ctypes.c_uint32, P]
     lib.kda_prefill_chunked_ex.restype = ctypes.c_int
+    lib.kda_prefill_chunked_at.argtypes = list(lib.kda_prefill_chunked.argtypes[:19]) + [
+        P, P, I32, P, P, SZ, ctypes.c_uint32, ctypes.c_uint32, P]
+    lib.kda_prefill_chunked_at.restype = ctypes.c_int
     lib.kda_decode_step.argtypes = [P, P, P, ctypes.c_int, P, P, I32, I32, I32, I32, P, P, P]
     lib.kda_decode_step.restype = ctypes.c_int
     lib.kda_decode_step_ex.argtypes = list(lib.kda_decode_step.argtypes[:-1]) + [
@@ -112,6 +116,18 @@ def prefill_ex_raw(q, k, v, dtype_code, g, beta, cu_seqlens, num_seqs, total_tok
                                          total_tokens, H, Dk, Dv, chunk_size, initial_state,
                                          final_state, ckpt_interval, ckpt_states, ckpt_rows, o,
                                          workspace, workspace_bytes, phases, frontend, stream)
+
+
+def prefill_at_raw(q, k, v, dtype_code, g, beta, cu_seqlens, num_seqs, total_tokens, H, Dk, Dv,
+                   chunk_size, initial_state, final_state, ckpt_interval, ckpt_states, ckpt_rows,
+                   o, pos_offsets, pos_values, num_pos, pos_states, workspace, workspace_bytes,
+                   phases, frontend, stream) -> int:
+    """Direct call of kda_prefill_chunked_at; returns the status."""
+    return load().kda_prefill_chunked_at(q, k, v, dtype_code, g, beta, cu_seqlens, num_seqs,
+                                         total_tokens, H, Dk, Dv, chunk_size, initial_state,
+                                         final_state, ckpt_interval, ckpt_states, ckpt_rows, o,
+                                         pos_offsets, pos_values, num_pos, pos_states, workspace,
+                                         workspace_bytes, phases, frontend, stream)
 
 
 def decode_ex_raw(q, k, v, dtype_code, g, beta, B, H, Dk, Dv, state, o, frontend,

@@ -66,6 +66,33 @@ def kda_prefill_chunked(q, k, v, g, beta, *, cu_seqlens=None, num_seqs=None,
     applied inside the kernels to raw q/k, g (= u) and beta (= logits)
     (kda_prefill_chunked_ex); 0 uses the inputs as given.
     Returns (o, final_state or None, ckpt_states or None)."""
+    o, fs, ck, _ = _prefill(q, k, v, g, beta, cu_seqlens, num_seqs, initial_state,
+                            output_final_state, final_state, ckpt_interval, num_checkpoints,
+                            ckpt_states, o, workspace, phases, frontend, None, None, None)
+    return o, fs, ck
+
+
+def kda_prefill_chunked_at(q, k, v, g, beta, pos_offsets, pos_values, *, pos_states=None,
+                           cu_seqlens=None, num_seqs=None, initial_state=None,
+                           output_final_state=True, final_state=None, ckpt_interval=0,
+                           num_checkpoints=None, ckpt_states=None, o=None, workspace=None,
+                           phases=B.PHASE_PREPARE | B.PHASE_SCAN, frontend=0):
+    """kda_prefill_chunked that also returns the states after the first P tokens
+    of a sequence for every requested P (include/kda.h, kda_prefill_chunked_at).
+
+    pos_offsets int32 [S+1] and pos_values int32 [num_pos] on the GPU: the
+    positions of sequence s are pos_values[pos_offsets[s]:pos_offsets[s+1]]
+    (non-decreasing token counts, 0 <= P <= L_s).
+    Returns (o, final_state or None, ckpt_states or None, pos_states)."""
+    return _prefill(q, k, v, g, beta, cu_seqlens, num_seqs, initial_state, output_final_state,
+                    final_state, ckpt_interval, num_checkpoints, ckpt_states, o, workspace,
+                    phases, frontend, pos_offsets, pos_values, pos_states)
+
+
+def _prefill(q, k, v, g, beta, cu_seqlens, num_seqs, initial_state, output_final_state,
+             final_state, ckpt_interval, num_checkpoints, ckpt_states, o, workspace, phases,
+             frontend, pos_offsets, pos_values, pos_states):
+    """Argument checks, output allocation and the call of the matching entry point."""
     dev = q.device
     N, H, Dk = q.shape
     Dv = v.shape[-1]
@@ -103,16 +130,29 @@ def kda_prefill_chunked(q, k, v, g, beta, *, cu_seqlens=None, num_seqs=None,
     if ckpt_interval > 0 and ckpt_states.numel() == 0:
         # zero checkpoint rows: any aligned non-null pointer is never written
         ck_ptr = workspace.data_ptr()
-    args = (_ptr(q), _ptr(k), _ptr(v), code, _ptr(g), _ptr(beta), _ptr(cu_seqlens), num_seqs, N,
+    head = (_ptr(q), _ptr(k), _ptr(v), code, _ptr(g), _ptr(beta), _ptr(cu_seqlens), num_seqs, N,
             H, Dk, Dv, CHUNK, _ptr(initial_state), _ptr(final_state), int(ckpt_interval), ck_ptr,
-            ck_rows, _ptr(o), _ptr(workspace), workspace.numel(), int(phases))
-    if frontend:
-        st = B.prefill_ex_raw(*args, int(frontend), _stream(dev))
+            ck_rows, _ptr(o))
+    tail = (_ptr(workspace), workspace.numel(), int(phases))
+    if pos_offsets is not None:
+        _check(pos_offsets, "pos_offsets", torch.int32, (num_seqs + 1,), dev)
+        _check(pos_values, "pos_values", torch.int32, None, dev)
+        npos = int(pos_values.numel())
+        if pos_states is None:
+            pos_states = torch.empty((npos, H, Dk, Dv), dtype=torch.float32, device=dev)
+        _check(pos_states, "pos_states", torch.float32, (npos, H, Dk, Dv), dev)
+        st = B.prefill_at_raw(*head, _ptr(pos_offsets), _ptr(pos_values), npos,
+                              _ptr(pos_states), *tail, int(frontend), _stream(dev))
+        where = "kda_prefill_chunked_at"
+    elif frontend:
+        st = B.prefill_ex_raw(*head, *tail, int(frontend), _stream(dev))
+        where = "kda_prefill_chunked_ex"
     else:
-        st = B.prefill_phases_raw(*args, _stream(dev))
+        st = B.prefill_phases_raw(*head, *tail, _stream(dev))
+        where = "kda_prefill_chunked"
     if st != B.KDA_OK:
-        raise B.KdaError(st, "kda_prefill_chunked")
-    return o, final_state, ckpt_states
+        raise B.KdaError(st, where)
+    return o, final_state, ckpt_states, pos_states
 
 
 def kda_decode_step(q, k, v, g, beta, state, o=None, frontend=0):

@@ -7,7 +7,7 @@
 
 namespace {
 
-constexpr int kVersion = 200;  // 0.2.0
+constexpr int kVersion = 300;  // 0.3.0
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -56,18 +56,27 @@ size_t kda_prefill_workspace_size(int64_t total_tokens, int32_t num_seqs, int32_
     return kda::prefill_workspace_bytes(total_tokens, num_seqs, H, Dk, Dv, in_dtype == KDA_BF16);
 }
 
-kda_status_t kda_prefill_chunked_ex(const void* q, const void* k, const void* v,
+kda_status_t kda_prefill_chunked_at(const void* q, const void* k, const void* v,
                                     kda_dtype_t in_dtype, const float* g, const float* beta,
                                     const int32_t* cu_seqlens, int32_t num_seqs,
                                     int64_t total_tokens, int32_t H, int32_t Dk, int32_t Dv,
                                     int32_t chunk_size, const float* initial_state,
                                     float* final_state, int64_t ckpt_interval,
                                     float* ckpt_states, int64_t ckpt_rows, float* o,
-                                    void* workspace, size_t workspace_bytes, uint32_t phases,
-                                    uint32_t frontend, hipStream_t stream) {
+                                    const int32_t* pos_offsets, const int32_t* pos_values,
+                                    int32_t num_pos, float* pos_states, void* workspace,
+                                    size_t workspace_bytes, uint32_t phases, uint32_t frontend,
+                                    hipStream_t stream) {
     if (phases == 0 || (phases & ~(KDA_PHASE_PREPARE | KDA_PHASE_SCAN)) != 0)
         return KDA_ERR_INVALID_ARG;
     if (frontend & ~kFrontMask) return KDA_ERR_INVALID_ARG;
+    if (num_pos < 0) return KDA_ERR_INVALID_ARG;
+    if (num_pos > 0) {
+        if (!pos_offsets || !pos_values || !pos_states) return KDA_ERR_INVALID_ARG;
+        if (!aligned(pos_offsets, 4) || !aligned(pos_values, 4) || !aligned(pos_states, 16))
+            return KDA_ERR_INVALID_ARG;
+        if ((int64_t)num_pos * H * 4 > (int64_t)INT32_MAX) return KDA_ERR_UNSUPPORTED;  // advance grid
+    }
     kda_status_t st = check_prefill_sizes(total_tokens, num_seqs, H, Dk, Dv, chunk_size, in_dtype);
     if (st != KDA_OK) return st;
     if (!cu_seqlens && num_seqs != 1) return KDA_ERR_INVALID_ARG;
@@ -107,7 +116,28 @@ kda_status_t kda_prefill_chunked_ex(const void* q, const void* k, const void* v,
     a.workspace_bytes = workspace_bytes;
     a.phases = phases;
     a.frontend = frontend;
+    if (num_pos > 0) {
+        a.pos.offsets = pos_offsets;
+        a.pos.values = pos_values;
+        a.pos.states = pos_states;
+        a.pos.num_pos = num_pos;
+    }
     return kda::launch_prefill(a, stream) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status_t kda_prefill_chunked_ex(const void* q, const void* k, const void* v,
+                                    kda_dtype_t in_dtype, const float* g, const float* beta,
+                                    const int32_t* cu_seqlens, int32_t num_seqs,
+                                    int64_t total_tokens, int32_t H, int32_t Dk, int32_t Dv,
+                                    int32_t chunk_size, const float* initial_state,
+                                    float* final_state, int64_t ckpt_interval,
+                                    float* ckpt_states, int64_t ckpt_rows, float* o,
+                                    void* workspace, size_t workspace_bytes, uint32_t phases,
+                                    uint32_t frontend, hipStream_t stream) {
+    return kda_prefill_chunked_at(q, k, v, in_dtype, g, beta, cu_seqlens, num_seqs, total_tokens,
+                                  H, Dk, Dv, chunk_size, initial_state, final_state,
+                                  ckpt_interval, ckpt_states, ckpt_rows, o, nullptr, nullptr, 0,
+                                  nullptr, workspace, workspace_bytes, phases, frontend, stream);
 }
 
 kda_status_t kda_prefill_chunked_phases(const void* q, const void* k, const void* v,

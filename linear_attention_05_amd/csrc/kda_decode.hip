@@ -251,6 +251,192 @@ hipError_t launch_dims(const void* q, const void* k, const void* v, bool bf16, c
     return hipGetLastError();
 }
 
+// ------------------------------------------------- position advance ----
+// Sum over the 16 lanes of a DPP row, left in every lane of the row: two
+// quad permutations, then rotations by 4 and 8 within the row (VALU lane
+// moves, no LDS round trip).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                                 CTRL, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float row_sum16(float x) {
+    x += dpp_mov<0xB1>(x);   // quad_perm [1, 0, 3, 2]
+    x += dpp_mov<0x4E>(x);   // quad_perm [2, 3, 0, 1]
+    x += dpp_mov<0x124>(x);  // row_ror:4
+    x += dpp_mov<0x128>(x);  // row_ror:8
+    return x;
+}
+
+// Sum over the whole wave, the same value in every lane: row sums, then the
+// four rows' values read as scalars and added in a fixed order.
+__device__ __forceinline__ float wave_sum64(float x) {
+    x = row_sum16(x);
+    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 0));
+    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 16));
+    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 32));
+    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 48));
+    return (r0 + r1) + (r2 + r3);
+}
+
+// States at arbitrary positions (kda_prefill_chunked_at): for a position of
+// P tokens the scan stored the state at the start of the chunk that holds P;
+// this kernel runs the remaining r = P mod 64 tokens of the recurrence on it,
+// in place (no outputs), one workgroup per (position, head, 32 columns),
+// with the state in registers. The same front-end bits apply as in the prefill that produced
+// the chunk-start state.
+template <int DK, int DV, bool BF16, bool L2>
+__global__ __launch_bounds__(kThreads) void advance_kernel(
+    const void* __restrict__ kin, const void* __restrict__ vin, const float* __restrict__ g,
+    const float* __restrict__ beta, const int32_t* __restrict__ cu, int num_seqs, int64_t N,
+    int H, PosArgs pos, unsigned front) {
+    // One workgroup = (position, head, 32 value columns); each wave owns 4
+    // whole columns (every key row), so the reduction S'^T k stays inside the
+    // wave and the token loop has no barrier. Lane l holds key rows l + 64 m.
+    constexpr int NCW = DV / 32;  // workgroups per (position, head)
+    constexpr int RPL = DK / 64;  // key rows per lane
+    static_assert(NCW * 32 == DV && RPL * 64 == DK && kWaves * 4 == 32, "bad advance tiling");
+
+    // the (at most 63) rows the position still needs, staged once: their loads
+    // are all in flight together instead of one token's worth per step
+    __shared__ __attribute__((aligned(16))) float s_g[63][DK], s_k[63][DK], s_v[63][32];
+    __shared__ float s_b[64];
+
+    const int t = threadIdx.x;
+    const int lane = t & 63, wave = t >> 6;
+    const unsigned wg = blockIdx.x;
+    const int cw = (int)(wg % NCW);
+    const int h = (int)((wg / NCW) % (unsigned)H);
+    const int j = (int)(wg / (NCW * (unsigned)H));
+    const int cbase = 32 * cw;          // this workgroup's first column
+    const int col = cbase + 4 * wave;   // this wave's four columns
+
+    // sequence of position j: the last s with offsets[s] <= j (clamped ranges)
+    int64_t st = 0, L = N;
+    if (cu) {
+        int lo = 0, hi = num_seqs - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (pos.offsets[mid] <= j) lo = mid;
+            else hi = mid - 1;
+        }
+        int64_t a = cu[lo], b = cu[lo + 1];
+        a = a < 0 ? 0 : (a > N ? N : a);
+        b = b < a ? a : (b > N ? N : b);
+        st = a;
+        L = b - a;
+    }
+    int64_t P = pos.values[j];
+    P = P < 0 ? 0 : (P > L ? L : P);
+    const int r = (int)(P % 64);
+    if (r == 0) return;  // the scan stored the exact state
+    const int64_t t0 = st + (P - r);
+    float* S = pos.states + ((size_t)j * H + h) * (size_t)(DK * DV);
+
+    f32x4 s[RPL];
+#pragma unroll
+    for (int m = 0; m < RPL; ++m)
+        s[m] = *reinterpret_cast<const f32x4*>(S + (int64_t)(lane + 64 * m) * DV + col);
+    // every staging load in flight at once: 4-element vectors, at most
+    // ceil(63 * DK / 4 / 512) = 4 of g and of k, 1 of v per thread
+    constexpr int NVK = (63 * DK / 4 + kThreads - 1) / kThreads;
+    f32x4 gv[NVK], kv[NVK], vv = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < NVK; ++u) {
+        const int idx = t + u * kThreads;  // (row, 4-channel group)
+        const int i = idx / (DK / 4), c = 4 * (idx % (DK / 4));
+        const int64_t e = ((t0 + i) * H + h) * DK + c;
+        if (i < r) {
+            gv[u] = *reinterpret_cast<const f32x4*>(g + e);
+            kv[u] = load_in4<BF16>(kin, e);
+        }
+    }
+    const int vi = t / 8, vc = 4 * (t % 8);  // (row, 4-column group) of the 32 columns
+    if (vi < r) vv = load_in4<BF16>(vin, ((t0 + vi) * H + h) * DV + cbase + vc);
+    float bt = t < r ? beta[(t0 + t) * H + h] : 0.f;
+#pragma unroll
+    for (int u = 0; u < NVK; ++u) {
+        const int idx = t + u * kThreads;
+        const int i = idx / (DK / 4), c = 4 * (idx % (DK / 4));
+        if (i < r) {
+            f32x4 gi = gv[u];
+            if (front & kFrontGate) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) gi[e] = -__expf(gi[e]);
+            }
+            *reinterpret_cast<f32x4*>(&s_g[i][c]) = gi;
+            *reinterpret_cast<f32x4*>(&s_k[i][c]) = kv[u];
+        }
+    }
+    if (vi < r) *reinterpret_cast<f32x4*>(&s_v[vi][vc]) = vv;
+    if (t < r) {
+        if (front & kFrontBeta) bt = 1.f / (1.f + __expf(-bt));
+        s_b[t] = bt;
+    }
+    __syncthreads();  // the only barrier: everything below reads LDS only
+
+    // token loop; each token's LDS operands are read one token ahead
+    float gn[RPL], kn_[RPL];
+    f32x4 vn;
+    float bn;
+    auto fetch = [&](int i) {
+#pragma unroll
+        for (int m = 0; m < RPL; ++m) {
+            gn[m] = s_g[i][lane + 64 * m];
+            kn_[m] = s_k[i][lane + 64 * m];
+        }
+        vn = *reinterpret_cast<const f32x4*>(&s_v[i][4 * wave]);
+        bn = s_b[i];
+    };
+    fetch(0);
+    for (int i = 0; i < r; ++i) {
+        float gc[RPL], kc[RPL];
+#pragma unroll
+        for (int m = 0; m < RPL; ++m) {
+            gc[m] = gn[m];
+            kc[m] = kn_[m];
+        }
+        const f32x4 vc = vn;
+        const float bc = bn;
+        fetch(i + 1 < r ? i + 1 : i);
+        if constexpr (L2) {  // key norm: every lane gets the same bits
+            float sk = 0.f;
+#pragma unroll
+            for (int m = 0; m < RPL; ++m) sk += kc[m] * kc[m];
+            const float inv = 1.f / sqrtf(wave_sum64(sk) + kL2Eps);
+#pragma unroll
+            for (int m = 0; m < RPL; ++m) kc[m] *= inv;
+        }
+        // decay, then S'^T k over the lane's rows and across the wave
+        f32x4 rr = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < RPL; ++m) {
+            s[m] *= __expf(gc[m]);
+            rr += s[m] * kc[m];
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) rr[e] = wave_sum64(rr[e]);
+        const f32x4 u = bc * (vc - rr);
+#pragma unroll
+        for (int m = 0; m < RPL; ++m) s[m] += kc[m] * u;
+    }
+#pragma unroll
+    for (int m = 0; m < RPL; ++m)
+        *reinterpret_cast<f32x4*>(S + (int64_t)(lane + 64 * m) * DV + col) = s[m];
+}
+
+template <int DK, int DV>
+hipError_t launch_advance_dims(const PrefillArgs& a, hipStream_t stream) {
+    const dim3 grid((unsigned)((int64_t)a.pos.num_pos * a.H * (DV / 32))), block(kThreads);
+    const bool l2 = (a.frontend & kFrontL2) != 0;
+    auto kern = a.bf16 ? (l2 ? &advance_kernel<DK, DV, true, true> : &advance_kernel<DK, DV, true, false>)
+                       : (l2 ? &advance_kernel<DK, DV, false, true> : &advance_kernel<DK, DV, false, false>);
+    hipLaunchKernelGGL(kern, grid, block, 0, stream, a.k, a.v, a.g, a.beta, a.cu_seqlens,
+                       a.num_seqs, a.total_tokens, a.H, a.pos, a.frontend);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_decode(const void* q, const void* k, const void* v, bool bf16,
@@ -261,6 +447,19 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, bool bf16,
     if (Dk == 128 && Dv == 64) return launch_dims<128, 64>(q, k, v, bf16, g, beta, B, H, state, o, front, stream);
     if (Dk == 64 && Dv == 128) return launch_dims<64, 128>(q, k, v, bf16, g, beta, B, H, state, o, front, stream);
     if (Dk == 64 && Dv == 64) return launch_dims<64, 64>(q, k, v, bf16, g, beta, B, H, state, o, front, stream);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace kda
+
+namespace kda {
+
+hipError_t launch_advance(const PrefillArgs& a, hipStream_t stream) {
+    if (a.pos.num_pos <= 0 || a.H <= 0) return hipSuccess;
+    if (a.Dk == 128 && a.Dv == 128) return launch_advance_dims<128, 128>(a, stream);
+    if (a.Dk == 128 && a.Dv == 64) return launch_advance_dims<128, 64>(a, stream);
+    if (a.Dk == 64 && a.Dv == 128) return launch_advance_dims<64, 128>(a, stream);
+    if (a.Dk == 64 && a.Dv == 64) return launch_advance_dims<64, 64>(a, stream);
     return hipErrorInvalidValue;
 }
 

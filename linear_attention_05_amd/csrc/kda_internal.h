@@ -21,6 +21,16 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, bool bf16,
                          float* state, float* o, unsigned frontend, hipStream_t stream);
 
 // ---- prefill --------------------------------------------------------------
+// States requested at arbitrary positions: the positions of sequence s are
+// values[offsets[s] .. offsets[s + 1]), each a token count P of that sequence
+// (the state after its first P tokens goes to states[j, h]).
+struct PosArgs {
+    const int32_t* offsets = nullptr;  // [num_seqs + 1]; null: no positions
+    const int32_t* values = nullptr;   // [num_pos]
+    float* states = nullptr;           // [num_pos, H, Dk, Dv]
+    int num_pos = 0;
+};
+
 struct PrefillArgs {
     const void* q;
     const void* k;
@@ -42,6 +52,7 @@ struct PrefillArgs {
     size_t workspace_bytes;
     unsigned phases;    // bit 0: prepare (prep + K1), bit 1: scan (K2)
     unsigned frontend;  // kFront* bits (0: inputs used as given)
+    PosArgs pos;
 };
 
 // Bytes of workspace the prefill path needs (0 if unsupported).
@@ -49,6 +60,10 @@ size_t prefill_workspace_bytes(int64_t total_tokens, int num_seqs, int H, int Dk
                                bool bf16);
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+
+// Advances each stored chunk-start state of a requested position by the
+// position's remaining P mod 64 tokens (implemented with the decode kernel).
+hipError_t launch_advance(const PrefillArgs& a, hipStream_t stream);
 
 // Upper bound on the number of 64-token chunks of a packed batch.
 inline int64_t max_chunks(int64_t total_tokens, int num_seqs) {

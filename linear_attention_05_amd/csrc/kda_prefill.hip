@@ -235,6 +235,56 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(const int32_t* __restric
     }
 }
 
+// Where a scan's chain stops to store a state: after every full checkpoint
+// interval, at the start of each chunk that holds a requested position (the
+// state after P tokens when P is a multiple of 64; otherwise the advance
+// kernel runs the remaining P mod 64 tokens), and at the end of the sequence.
+// Positions are clamped into [0, L] and list indices into [0, num_pos];
+// out-of-order positions still make progress (every stop consumes an entry
+// or reaches the end). All values are uniform over the workgroup.
+struct StopWalk {
+    const int32_t* val;
+    int pj, pe, ick, next_iv, nch;
+    int64_t L;
+    __device__ StopWalk(const PosArgs& p, int seq, int64_t len, int64_t interval, int nchunks)
+        : val(p.values), pj(0), pe(0), ick(interval > 0 ? (int)(interval / C) : 0),
+          next_iv(interval > 0 ? (int)(interval / C) : 0), nch(nchunks), L(len) {
+        if (p.offsets) {
+            const int a = p.offsets[seq], b = p.offsets[seq + 1];
+            pj = a < 0 ? 0 : (a > p.num_pos ? p.num_pos : a);
+            pe = b < pj ? pj : (b > p.num_pos ? p.num_pos : b);
+        }
+    }
+    __device__ int pos_chunk(int j) const {
+        int64_t P = val[j];
+        P = P < 0 ? 0 : (P > L ? L : P);
+        return (int)(P / C);
+    }
+    __device__ int next() const {
+        int s = nch;
+        if (ick > 0 && next_iv < s) s = next_iv;
+        if (pj < pe) {
+            const int c = pos_chunk(pj);
+            if (c < s) s = c;
+        }
+        return s;
+    }
+    // a checkpoint interval ends at this stop (true if it is a full one)
+    __device__ bool take_interval(int stop) {
+        if (ick == 0 || stop != next_iv) return false;
+        next_iv += ick;
+        return (int64_t)stop * C <= L;
+    }
+    // the next requested position whose chunk starts at this stop
+    __device__ bool take_position(int stop, int& j) {
+        if (pj < pe && pos_chunk(pj) == stop) {
+            j = pj++;
+            return true;
+        }
+        return false;
+    }
+};
+
 // Locate chunk ci: first token and length (len <= 0: no such chunk).
 __device__ __forceinline__ void locate_chunk(int ci, const int32_t* cu, const int32_t* chunk_start,
                                              int num_seqs, int64_t N, int64_t& t0, int& len) {
@@ -777,7 +827,8 @@ __global__ __launch_bounds__(kThreads) void k2_scan_kernel(
     const int32_t* __restrict__ chunk_start, const int32_t* __restrict__ ckpt_base, int npairs,
     int64_t N, int H, int64_t max_chunks, const unsigned char* __restrict__ handoff,
     const float* __restrict__ s0, float* __restrict__ sfinal, int64_t interval,
-    float* __restrict__ ckpt, int64_t ckpt_rows, float* __restrict__ o, float* __restrict__ sink) {
+    float* __restrict__ ckpt, int64_t ckpt_rows, PosArgs pos, float* __restrict__ o,
+    float* __restrict__ sink) {
     using M = Mma<BF16>;
     using E = typename M::E;
     using Frag = typename M::Frag;
@@ -1004,25 +1055,31 @@ __global__ __launch_bounds__(kThreads) void k2_scan_kernel(
     // Chunks run in segments that end on checkpoint boundaries, so the
     // branch-free chunk loop never stores a state; each checkpoint is written
     // between segments. Without checkpoints there is one segment.
-    const int ick = interval > 0 ? (int)(interval / C) : nch;  // chunks per segment
+    StopWalk sw(pos, seq, L, interval, nch);
     int64_t cidx = cpbase;
     Ops b0, b1, b2;
-    for (int seg0 = 0; seg0 < nch; seg0 += ick) {
-        const int seg1 = seg0 + ick < nch ? seg0 + ick : nch;
-        load_all(b0, seg0);
-        load_all(b1, seg0 + 1 < seg1 ? seg0 + 1 : seg0);
-        for (int n = seg0; n < seg1; n += 3) {
-            step(b0, n, b2, n + 2 < seg1 ? n + 2 : seg1 - 1);
-            if (n + 1 >= seg1) break;
-            step(b1, n + 1, b0, n + 3 < seg1 ? n + 3 : seg1 - 1);
-            if (n + 2 >= seg1) break;
-            step(b2, n + 2, b1, n + 4 < seg1 ? n + 4 : seg1 - 1);
+    for (int n0 = 0;;) {
+        const int stop = sw.next();
+        if (stop > n0) {
+            const int seg0 = n0, seg1 = stop;
+            load_all(b0, seg0);
+            load_all(b1, seg0 + 1 < seg1 ? seg0 + 1 : seg0);
+            for (int n = seg0; n < seg1; n += 3) {
+                step(b0, n, b2, n + 2 < seg1 ? n + 2 : seg1 - 1);
+                if (n + 1 >= seg1) break;
+                step(b1, n + 1, b0, n + 3 < seg1 ? n + 3 : seg1 - 1);
+                if (n + 2 >= seg1) break;
+                step(b2, n + 2, b1, n + 4 < seg1 ? n + 4 : seg1 - 1);
+            }
+            n0 = stop;
         }
-        // a full segment ends exactly ick * 64 tokens later: checkpoint
-        if (interval > 0 && (int64_t)seg1 * C <= L && seg1 - seg0 == ick) {
+        if (sw.take_interval(stop)) {  // a full interval ends here: checkpoint
             if (cidx < ckpt_rows) store_state(ckpt + (cidx * H + h) * (size_t)DK * DV);
             ++cidx;
         }
+        for (int j; sw.take_position(stop, j);)
+            store_state(pos.states + ((size_t)j * H + h) * DK * DV);
+        if (stop >= nch) break;
     }
 
     if (sfinal) store_state(sfinal + sbase);
@@ -1054,7 +1111,8 @@ __global__ __launch_bounds__(192) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int32_t* __restrict__ chunk_start, const int32_t* __restrict__ ckpt_base, int npairs,
     int64_t N, int H, int64_t max_chunks, const unsigned char* handoff,
     const float* __restrict__ s0, float* __restrict__ sfinal, int64_t interval,
-    float* __restrict__ ckpt, int64_t ckpt_rows, float* __restrict__ o, float* __restrict__ sink) {
+    float* __restrict__ ckpt, int64_t ckpt_rows, PosArgs pos, float* __restrict__ o,
+    float* __restrict__ sink) {
     using M = Mma<true>;
     using E = _Float16;
     using Frag = half8;
@@ -1205,18 +1263,25 @@ __global__ __launch_bounds__(192) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         // Chunks run in segments that end on checkpoint boundaries, so the
         // chunk loop itself never branches; each checkpoint is stored between
         // segments. Without checkpoints there is one segment.
-        const int ick = interval > 0 ? (int)(interval / C) : (nch > 0 ? nch : 1);
+        StopWalk sw(pos, seq, L, interval, nch);
         int64_t cidx = ckpt_base ? ckpt_base[seq] : 0;
-        for (int seg0 = 0; seg0 < nch; seg0 += ick) {
-            const int seg1 = seg0 + ick < nch ? seg0 + ick : nch;
-            for (int n = seg0; n < seg1; ++n) step(n, clampc(n + 1));
-            if (interval > 0 && (int64_t)seg1 * C <= L && seg1 - seg0 == ick) {
+        for (int n = 0;;) {
+            const int stop = sw.next();
+            for (; n < stop; ++n) step(n, clampc(n + 1));
+            bool stored = false;
+            if (sw.take_interval(stop)) {
                 if (cidx < ckpt_rows) store_state(ckpt + (cidx * H + h) * (size_t)DK * DV);
                 ++cidx;
-                // drain the checkpoint stores here, so that the chunk loop's
-                // memory waits need not allow for them (they are rare)
-                __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+                stored = true;
             }
+            for (int j; sw.take_position(stop, j);) {
+                store_state(pos.states + ((size_t)j * H + h) * DK * DV);
+                stored = true;
+            }
+            // drain the state stores here, so that the chunk loop's memory
+            // waits need not allow for them (they are rare)
+            if (stored) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+            if (stop >= nch) break;
         }
         if (sfinal) store_state(sfinal + sbase);
     } else if (wave == 2) {
@@ -1429,7 +1494,8 @@ __global__ __launch_bounds__(320) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
     const int32_t* __restrict__ chunk_start, const int32_t* __restrict__ ckpt_base, int npairs,
     int64_t N, int H, int64_t max_chunks, const unsigned char* handoff,
     const float* __restrict__ s0, float* __restrict__ sfinal, int64_t interval,
-    float* __restrict__ ckpt, int64_t ckpt_rows, float* __restrict__ o, float* __restrict__ sink) {
+    float* __restrict__ ckpt, int64_t ckpt_rows, PosArgs pos, float* __restrict__ o,
+    float* __restrict__ sink) {
     using M = Mma<true>;
     using E = _Float16;
     using Frag = half8;
@@ -1589,16 +1655,23 @@ __global__ __launch_bounds__(320) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
         // Chunks run in segments that end on checkpoint boundaries, so the
         // chunk loop itself never branches; each checkpoint is stored between
         // segments. Without checkpoints there is one segment.
-        const int ick = interval > 0 ? (int)(interval / C) : (nch > 0 ? nch : 1);
+        StopWalk sw(pos, seq, L, interval, nch);
         int64_t cidx = ckpt_base ? ckpt_base[seq] : 0;
-        for (int seg0 = 0; seg0 < nch; seg0 += ick) {
-            const int seg1 = seg0 + ick < nch ? seg0 + ick : nch;
-            for (int n = seg0; n < seg1; ++n) step(n);
-            if (interval > 0 && (int64_t)seg1 * C <= L && seg1 - seg0 == ick) {
+        for (int n = 0;;) {
+            const int stop = sw.next();
+            for (; n < stop; ++n) step(n);
+            bool stored = false;
+            if (sw.take_interval(stop)) {
                 if (cidx < ckpt_rows) store_state(ckpt + (cidx * H + h) * (size_t)DK * DV);
                 ++cidx;
-                __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): drain the (rare) checkpoint stores
+                stored = true;
             }
+            for (int j; sw.take_position(stop, j);) {
+                store_state(pos.states + ((size_t)j * H + h) * DK * DV);
+                stored = true;
+            }
+            if (stored) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): drain the (rare) state stores
+            if (stop >= nch) break;
         }
         if (sfinal) store_state(sfinal + sbase);
     } else if (wave == NCB + 2) {
@@ -1855,7 +1928,7 @@ void launch_scan(const PrefillArgs& a, const Plan& p, int npairs, hipStream_t st
                        a.v, a.cu_seqlens, varlen ? p.order : nullptr,
                        varlen ? p.chunk_start : nullptr, varlen ? p.ckpt_base : nullptr, npairs,
                        a.total_tokens, a.H, p.max_chunks, p.handoff, a.initial_state, a.final_state,
-                       a.ckpt_interval, a.ckpt_states, a.ckpt_rows, a.o, p.sink);
+                       a.ckpt_interval, a.ckpt_states, a.ckpt_rows, a.pos, a.o, p.sink);
 }
 
 // Three-wave scan: one workgroup per (pair, 16 columns). When there are no
@@ -1882,7 +1955,7 @@ void launch_trio(const PrefillArgs& a, const Plan& p, int npairs, int cus, int l
                        a.v, a.cu_seqlens, varlen ? p.order : nullptr,
                        varlen ? p.chunk_start : nullptr, varlen ? p.ckpt_base : nullptr, npairs,
                        a.total_tokens, a.H, p.max_chunks, p.handoff, a.initial_state, a.final_state,
-                       a.ckpt_interval, a.ckpt_states, a.ckpt_rows, a.o, p.sink);
+                       a.ckpt_interval, a.ckpt_states, a.ckpt_rows, a.pos, a.o, p.sink);
 }
 
 // Five-wave scan: one workgroup per (pair, 32 columns), one per CU (its LDS
@@ -1897,7 +1970,7 @@ void launch_quad(const PrefillArgs& a, const Plan& p, int npairs, hipStream_t st
                        a.v, a.cu_seqlens, varlen ? p.order : nullptr,
                        varlen ? p.chunk_start : nullptr, varlen ? p.ckpt_base : nullptr, npairs,
                        a.total_tokens, a.H, p.max_chunks, p.handoff, a.initial_state, a.final_state,
-                       a.ckpt_interval, a.ckpt_states, a.ckpt_rows, a.o, p.sink);
+                       a.ckpt_interval, a.ckpt_states, a.ckpt_rows, a.pos, a.o, p.sink);
 }
 
 template <int DK, int DV, bool BF16>
@@ -1952,6 +2025,11 @@ hipError_t launch_typed(const PrefillArgs& a, hipStream_t stream) {
             case kQuad: launch_quad<DK, DV>(a, p, npairs, stream); break;
             case kNt4: launch_scan<DK, DV, 4, BF16>(a, p, npairs, stream); break;
             default: launch_scan<DK, DV, 1, BF16>(a, p, npairs, stream); break;
+        }
+        if (a.pos.num_pos > 0) {  // finish the states of positions inside a chunk
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+            return launch_advance(a, stream);
         }
     }
     return hipGetLastError();

@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert B.version() >= 200  # 0.2.0: the *_ex entry points
+    assert B.version() >= 300  # 0.3.0: kda_prefill_chunked_at
     for s in range(5):
         assert B.status_string(s).startswith("KDA_")
     assert "unknown" in B.status_string(99)
@@ -116,6 +116,22 @@ def test_decode_ex_validation(front, kw, status):
     a.update(kw)
     st = B.decode_ex_raw(A, A, A, B.KDA_BF16, A, A, a["B"], 2, a["Dk"], 128, a["st"], A, front,
                          None)
+    assert st == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(npos=-1), INV),
+    (dict(offs=None), INV), (dict(vals=None), INV), (dict(ps=None), INV),
+    (dict(offs=A + 2), INV), (dict(vals=A + 1), INV), (dict(ps=A + 8), INV),
+    (dict(front=16), INV), (dict(phases=0), INV), (dict(Dk=96), UNS), (dict(wsb=1000), WS),
+    (dict(npos=2 ** 30), UNS),                         # num_pos * H overflows int32
+])
+def test_prefill_at_validation(kw, status):
+    a = dict(npos=3, offs=A, vals=A, ps=A, front=0, phases=3, Dk=128, wsb=10 ** 12)
+    a.update(kw)
+    st = B.prefill_at_raw(A, A, A, B.KDA_BF16, A, A, None, 1, 256, 2, a["Dk"], 128, 64, None, A,
+                          0, None, 0, A, a["offs"], a["vals"], a["npos"], a["ps"], A, a["wsb"],
+                          a["phases"], a["front"], None)
     assert st == status
 
 
