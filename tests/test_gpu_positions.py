@@ -8,7 +8,7 @@ import pytest
 from helpers import assert_parity, dev_tensor
 from oracle import frontend as fe
 from oracle import recurrence
-from synth import make_prefill
+from synth import make_prefill, make_workload
 from synth.inputs import PrefillInputs
 
 pytestmark = pytest.mark.gpu
@@ -35,7 +35,10 @@ def gpu_at(x, positions, *, front=0, phases=3, workspace=None, o=None, final_sta
 
 def oracle_states(x, positions, front=0, units=None):
     """State after the first P tokens of each listed position, [num_pos, H, Dk, Dv]."""
-    q, k, v, g, beta = fe.apply(x.q, x.k, x.v, x.g, x.beta, front)
+    if front:
+        q, k, v, g, beta = fe.apply(x.q, x.k, x.v, x.g, x.beta, front)
+    else:  # storage dtypes straight to the oracle (no fp64 copies of large inputs)
+        q, k, v, g, beta = x.q, x.k, x.v, x.g, x.beta
     out = []
     for s, plist in enumerate(positions):
         a = int(x.cu_seqlens[s])
@@ -138,3 +141,51 @@ def test_headline_shape_positions_sampled():
     for _, h, cb in units:
         cols = slice(16 * cb, 16 * cb + 16)
         assert_parity(ps[:, h, :, cols], ref[:, h, :, cols], "bf16", f"head {h} cols {cb}")
+
+
+def _sampled(x, positions, units, what):
+    o, fs, ck, ps = gpu_at(x, positions)
+    ref = oracle_states(x, positions, units=units)
+    ps = ps.cpu().numpy()
+    for _, h, cb in units:
+        cols = slice(16 * cb, 16 * cb + 16)
+        assert_parity(ps[:, h, :, cols], ref[:, h, :, cols], "bf16", f"{what} head {h} cols {cb}")
+    return o, fs, ck
+
+
+def test_long_context_positions_with_checkpoints_sampled():
+    """T = 147,456 with checkpoints every 32,768 tokens (stops merged with the
+    checkpoint segments), positions inside and on chunk boundaries."""
+    x = make_workload(2)
+    units = np.array([(0, 3, 1), (0, 30, 6)])
+    _, _, ck = _sampled(x, [[5000, 32768, 70001, 147455]], units, "long context")
+    # the checkpoints of the same call
+    r = recurrence.prefill(x.q, x.k, x.v, x.g, x.beta, x.cu_seqlens, ckpt_interval=x.ckpt_interval,
+                           units=units)
+    ck = ck.cpu().numpy()
+    for _, h, cb in units:
+        cols = slice(16 * cb, 16 * cb + 16)
+        assert_parity(ck[:, h, :, cols], r["ckpt"][:, h, :, cols], "bf16", f"checkpoints head {h}")
+
+
+def test_varlen_workload_positions_sampled():
+    """64 packed sequences (the 64-column four-wave scan at this size), one
+    position in every eighth sequence."""
+    x = make_workload(3)
+    positions = [[] for _ in range(x.num_seqs)]
+    for s in range(0, x.num_seqs, 8):
+        positions[s] = [x.lengths[s] // 3]
+    units_by_seq = [(s, 5, 2) for s in range(0, x.num_seqs, 8)]
+    o, fs, ck, ps = gpu_at(x, positions)
+    ps = ps.cpu().numpy()
+    for j, (s, h, cb) in enumerate(units_by_seq):
+        one = PrefillInputs(x.dtype, x.H, x.Dk, x.Dv, [x.lengths[s]],
+                            x.q[x.cu_seqlens[s]:x.cu_seqlens[s + 1]],
+                            x.k[x.cu_seqlens[s]:x.cu_seqlens[s + 1]],
+                            x.v[x.cu_seqlens[s]:x.cu_seqlens[s + 1]],
+                            x.g[x.cu_seqlens[s]:x.cu_seqlens[s + 1]],
+                            x.beta[x.cu_seqlens[s]:x.cu_seqlens[s + 1]],
+                            x.initial_state[s:s + 1])
+        ref = oracle_states(one, [positions[s]], units=np.array([(0, h, cb)]))
+        cols = slice(16 * cb, 16 * cb + 16)
+        assert_parity(ps[j, h, :, cols], ref[0, h, :, cols], "bf16", f"varlen seq {s}")
