@@ -269,48 +269,37 @@ __device__ __forceinline__ float row_sum16(float x) {
     return x;
 }
 
-// Sum over the whole wave, the same value in every lane: row sums, then the
-// four rows' values read as scalars and added in a fixed order.
-__device__ __forceinline__ float wave_sum64(float x) {
-    x = row_sum16(x);
-    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 0));
-    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 16));
-    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 32));
-    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 48));
-    return (r0 + r1) + (r2 + r3);
-}
-
 // States at arbitrary positions (kda_prefill_chunked_at): for a position of
 // P tokens the scan stored the state at the start of the chunk that holds P;
 // this kernel runs the remaining r = P mod 64 tokens of the recurrence on it,
-// in place (no outputs), one workgroup per (position, head, 32 columns),
-// with the state in registers. The same front-end bits apply as in the prefill that produced
+// in place (no outputs), one workgroup per (position, head), with the state
+// in registers. The same front-end bits apply as in the prefill that produced
 // the chunk-start state.
 template <int DK, int DV, bool BF16, bool L2>
 __global__ __launch_bounds__(kThreads) void advance_kernel(
     const void* __restrict__ kin, const void* __restrict__ vin, const float* __restrict__ g,
     const float* __restrict__ beta, const int32_t* __restrict__ cu, int num_seqs, int64_t N,
     int H, PosArgs pos, unsigned front) {
-    // One workgroup = (position, head, 32 value columns); each wave owns 4
-    // whole columns (every key row), so the reduction S'^T k stays inside the
-    // wave and the token loop has no barrier. Lane l holds key rows l + 64 m.
-    constexpr int NCW = DV / 32;  // workgroups per (position, head)
-    constexpr int RPL = DK / 64;  // key rows per lane
-    static_assert(NCW * 32 == DV && RPL * 64 == DK && kWaves * 4 == 32, "bad advance tiling");
+    // One workgroup per (position, head). Wave w owns value columns
+    // w * CPW .. +CPW-1 (every key row); lane = 16 * cgl + rgl holds the four
+    // columns of group cgl for the rows rgl + 16 m, so the reduction S'^T k
+    // over rows is one 16-lane DPP row sum and the token loop has no barrier.
+    constexpr int CPW = DV / kWaves;  // columns per wave (16 or 8)
+    constexpr int CGW = CPW / 4;      // 4-column groups per wave (4 or 2)
+    constexpr int RPL = DK / 16;      // rows per lane (8 or 4)
+    static_assert(CGW * 4 == CPW && RPL * 16 == DK && CGW * 16 <= 64, "bad advance tiling");
 
     // the (at most 63) rows the position still needs, staged once: their loads
     // are all in flight together instead of one token's worth per step
-    __shared__ __attribute__((aligned(16))) float s_g[63][DK], s_k[63][DK], s_v[63][32];
+    __shared__ __attribute__((aligned(16))) float s_g[63][DK], s_k[63][DK], s_v[63][DV];
     __shared__ float s_b[64];
 
     const int t = threadIdx.x;
     const int lane = t & 63, wave = t >> 6;
-    const unsigned wg = blockIdx.x;
-    const int cw = (int)(wg % NCW);
-    const int h = (int)((wg / NCW) % (unsigned)H);
-    const int j = (int)(wg / (NCW * (unsigned)H));
-    const int cbase = 32 * cw;          // this workgroup's first column
-    const int col = cbase + 4 * wave;   // this wave's four columns
+    const int cgl = lane >> 4, rgl = lane & 15;
+    const bool active = cgl < CGW;  // DV = 64: lanes 32..63 mirror 0..31 and store nothing
+    const int col = wave * CPW + 4 * (active ? cgl : 0);
+    const int j = (int)(blockIdx.x / (unsigned)H), h = (int)(blockIdx.x % (unsigned)H);
 
     // sequence of position j: the last s with offsets[s] <= j (clamped ranges)
     int64_t st = 0, L = N;
@@ -337,11 +326,12 @@ __global__ __launch_bounds__(kThreads) void advance_kernel(
     f32x4 s[RPL];
 #pragma unroll
     for (int m = 0; m < RPL; ++m)
-        s[m] = *reinterpret_cast<const f32x4*>(S + (int64_t)(lane + 64 * m) * DV + col);
+        s[m] = *reinterpret_cast<const f32x4*>(S + (int64_t)(rgl + 16 * m) * DV + col);
     // every staging load in flight at once: 4-element vectors, at most
-    // ceil(63 * DK / 4 / 512) = 4 of g and of k, 1 of v per thread
+    // ceil(63 * D / 4 / 512) = 4 of each tensor per thread
     constexpr int NVK = (63 * DK / 4 + kThreads - 1) / kThreads;
-    f32x4 gv[NVK], kv[NVK], vv = {0.f, 0.f, 0.f, 0.f};
+    constexpr int NVV = (63 * DV / 4 + kThreads - 1) / kThreads;
+    f32x4 gv[NVK], kv[NVK], vv[NVV];
 #pragma unroll
     for (int u = 0; u < NVK; ++u) {
         const int idx = t + u * kThreads;  // (row, 4-channel group)
@@ -352,8 +342,12 @@ __global__ __launch_bounds__(kThreads) void advance_kernel(
             kv[u] = load_in4<BF16>(kin, e);
         }
     }
-    const int vi = t / 8, vc = 4 * (t % 8);  // (row, 4-column group) of the 32 columns
-    if (vi < r) vv = load_in4<BF16>(vin, ((t0 + vi) * H + h) * DV + cbase + vc);
+#pragma unroll
+    for (int u = 0; u < NVV; ++u) {
+        const int idx = t + u * kThreads;
+        const int i = idx / (DV / 4), c = 4 * (idx % (DV / 4));
+        if (i < r) vv[u] = load_in4<BF16>(vin, ((t0 + i) * H + h) * DV + c);
+    }
     float bt = t < r ? beta[(t0 + t) * H + h] : 0.f;
 #pragma unroll
     for (int u = 0; u < NVK; ++u) {
@@ -369,7 +363,12 @@ __global__ __launch_bounds__(kThreads) void advance_kernel(
             *reinterpret_cast<f32x4*>(&s_k[i][c]) = kv[u];
         }
     }
-    if (vi < r) *reinterpret_cast<f32x4*>(&s_v[vi][vc]) = vv;
+#pragma unroll
+    for (int u = 0; u < NVV; ++u) {
+        const int idx = t + u * kThreads;
+        const int i = idx / (DV / 4), c = 4 * (idx % (DV / 4));
+        if (i < r) *reinterpret_cast<f32x4*>(&s_v[i][c]) = vv[u];
+    }
     if (t < r) {
         if (front & kFrontBeta) bt = 1.f / (1.f + __expf(-bt));
         s_b[t] = bt;
@@ -383,10 +382,10 @@ __global__ __launch_bounds__(kThreads) void advance_kernel(
     auto fetch = [&](int i) {
 #pragma unroll
         for (int m = 0; m < RPL; ++m) {
-            gn[m] = s_g[i][lane + 64 * m];
-            kn_[m] = s_k[i][lane + 64 * m];
+            gn[m] = s_g[i][rgl + 16 * m];
+            kn_[m] = s_k[i][rgl + 16 * m];
         }
-        vn = *reinterpret_cast<const f32x4*>(&s_v[i][4 * wave]);
+        vn = *reinterpret_cast<const f32x4*>(&s_v[i][col]);
         bn = s_b[i];
     };
     fetch(0);
@@ -400,15 +399,15 @@ __global__ __launch_bounds__(kThreads) void advance_kernel(
         const f32x4 vc = vn;
         const float bc = bn;
         fetch(i + 1 < r ? i + 1 : i);
-        if constexpr (L2) {  // key norm: every lane gets the same bits
+        if constexpr (L2) {  // key norm over the 16 row groups (every lane: same bits)
             float sk = 0.f;
 #pragma unroll
             for (int m = 0; m < RPL; ++m) sk += kc[m] * kc[m];
-            const float inv = 1.f / sqrtf(wave_sum64(sk) + kL2Eps);
+            const float inv = 1.f / sqrtf(row_sum16(sk) + kL2Eps);
 #pragma unroll
             for (int m = 0; m < RPL; ++m) kc[m] *= inv;
         }
-        // decay, then S'^T k over the lane's rows and across the wave
+        // decay, then S'^T k over the lane's rows and the DPP row's 16 row groups
         f32x4 rr = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int m = 0; m < RPL; ++m) {
@@ -416,19 +415,21 @@ __global__ __launch_bounds__(kThreads) void advance_kernel(
             rr += s[m] * kc[m];
         }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) rr[e] = wave_sum64(rr[e]);
+        for (int e = 0; e < 4; ++e) rr[e] = row_sum16(rr[e]);
         const f32x4 u = bc * (vc - rr);
 #pragma unroll
         for (int m = 0; m < RPL; ++m) s[m] += kc[m] * u;
     }
+    if (active) {
 #pragma unroll
-    for (int m = 0; m < RPL; ++m)
-        *reinterpret_cast<f32x4*>(S + (int64_t)(lane + 64 * m) * DV + col) = s[m];
+        for (int m = 0; m < RPL; ++m)
+            *reinterpret_cast<f32x4*>(S + (int64_t)(rgl + 16 * m) * DV + col) = s[m];
+    }
 }
 
 template <int DK, int DV>
 hipError_t launch_advance_dims(const PrefillArgs& a, hipStream_t stream) {
-    const dim3 grid((unsigned)((int64_t)a.pos.num_pos * a.H * (DV / 32))), block(kThreads);
+    const dim3 grid((unsigned)((int64_t)a.pos.num_pos * a.H)), block(kThreads);
     const bool l2 = (a.frontend & kFrontL2) != 0;
     auto kern = a.bf16 ? (l2 ? &advance_kernel<DK, DV, true, true> : &advance_kernel<DK, DV, true, false>)
                        : (l2 ? &advance_kernel<DK, DV, false, true> : &advance_kernel<DK, DV, false, false>);
