@@ -106,7 +106,8 @@ size_t kda_prefill_workspace_size(int64_t total_tokens, int32_t num_seqs, int32_
  *                      NULL means one sequence of total_tokens (num_seqs must
  *                      be 1). Zero-length sequences are allowed: their final
  *                      state equals their initial state.
- *   num_seqs, total_tokens, H, Dk, Dv   sizes; Dk, Dv in {64, 128}
+ *   num_seqs, total_tokens, H, Dk, Dv   sizes; Dk, Dv in {64, 128};
+ *                      H * max(Dk, Dv) * 64 <= 2^31 - 1 (else KDA_ERR_UNSUPPORTED)
  *   chunk_size         must be 64
  *   initial_state      [num_seqs, H, Dk, Dv] fp32 or NULL (zeros)
  *   final_state        [num_seqs, H, Dk, Dv] fp32 or NULL (not written)

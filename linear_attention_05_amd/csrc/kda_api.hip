@@ -29,6 +29,9 @@ kda_status_t check_prefill_sizes(int64_t total_tokens, int32_t num_seqs, int32_t
         return KDA_ERR_UNSUPPORTED;
     if (!supported_dim(Dk) || !supported_dim(Dv) || chunk_size != kda::kChunk)
         return KDA_ERR_UNSUPPORTED;
+    // the kernels address a chunk's rows with 32-bit offsets (r * H * D, r < 64)
+    if ((int64_t)H * (Dk > Dv ? Dk : Dv) * kda::kChunk > (int64_t)INT32_MAX)
+        return KDA_ERR_UNSUPPORTED;
     return KDA_OK;
 }
 

@@ -74,6 +74,7 @@ def prefill(**kw):
     (dict(beta=None), INV), (dict(o=None), INV),
     (dict(N=-5), INV), (dict(H=0), INV), (dict(S=0), INV), (dict(dt=3), INV),
     (dict(Dk=96), UNS), (dict(Dv=32), UNS), (dict(chunk=128), UNS), (dict(N=2 ** 31), UNS),
+    (dict(H=2 ** 18), UNS),                            # H * D * 64 past 32-bit row offsets
     (dict(S=2), INV),                                  # several sequences need cu_seqlens
     (dict(ci=-64), INV), (dict(ci=96), UNS),           # interval not a multiple of 64
     (dict(ci=128), INV),                               # interval without a buffer
