@@ -205,6 +205,56 @@ def cpu_baseline(x, target_s=10.0):
                 seconds=spent)
 
 
+def bench_few_heads(H=4, T=65536, D=128, reps=5):
+    """One sequence with few heads (a head-sharded layer's per-GPU share): the
+    chunk-parallel scan (one call) against the plain scan (prepare and scan as
+    two calls on the same inputs), medians over reps, inputs resident."""
+    import numpy as np
+    import torch
+    import linear_attention_05_amd as K
+    from linear_attention_05_amd import _binding as B
+    from linear_attention_05_amd import accounting as acc
+    from synth import make_prefill
+
+    x = make_prefill([T], H, D, D, "bf16", 4242, init_state=True)
+    args = [dev(a) for a in (x.q, x.k, x.v, x.g, x.beta)]
+    s0 = dev(x.initial_state)
+    o = torch.empty(T, H, D, device="cuda")
+    fs = torch.empty(1, H, D, D, device="cuda")
+    ws = torch.empty(K.kda_prefill_workspace_size(T, 1, H, D, D), dtype=torch.uint8, device="cuda")
+
+    def split():
+        K.kda_prefill_chunked(*args, initial_state=s0, final_state=fs, o=o, workspace=ws)
+
+    def plain():
+        for p in (B.PHASE_PREPARE, B.PHASE_SCAN):
+            K.kda_prefill_chunked(*args, initial_state=s0, final_state=fs, o=o, workspace=ws,
+                                  phases=p)
+
+    def timed(fn):
+        fn()
+        times = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        return float(np.median(times))
+
+    ms_split, ms_plain = timed(split), timed(plain)
+    byts = acc.prefill_compulsory_bytes(T, H, D, D, 2, 1, 1)
+    return dict(workload=f"prefill B=1 H={H} T={T} D={D} bf16, S0 and final state",
+                segments=K.kda_prefill_scan_segments(T, 1, H, D, D),
+                split_ms=round(ms_split, 4), plain_ms=round(ms_plain, 4),
+                split_mtok_s=round(T / (ms_split * 1e-3) / 1e6, 3),
+                plain_mtok_s=round(T / (ms_plain * 1e-3) / 1e6, 3),
+                speedup=round(ms_plain / ms_split, 3),
+                split_path_roofline_frac=round(byts / (ms_split * 1e-3) / 8e12, 4))
+
+
 def bench_prefill_workload(idx, reps=3):
     """Time one whole prefill call of another workload (long-context with
     checkpoints, or packed varlen): median over reps, inputs resident."""
@@ -517,6 +567,7 @@ def main():
                         "roofline": out["decode"]["roofline"]})
     if args.only in ("all", "prefill") and not args.no_extra_workloads:
         out["prefill_workloads"] = [bench_prefill_workload(2), bench_prefill_workload(3)]
+        out["few_heads"] = [bench_few_heads(4), bench_few_heads(1)]
     if args.only == "all" and not args.no_extra_workloads:
         out["frontend"] = bench_frontend()
         out["positions"] = bench_positions()

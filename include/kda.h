@@ -83,10 +83,35 @@ const char *kda_status_string(kda_status_t status);
 /*
  * Bytes of device workspace kda_prefill_chunked needs for these sizes.
  * Returns 0 when the sizes are invalid or unsupported (the same checks as
- * kda_prefill_chunked). The size depends only on the arguments, so one
- * allocation can be reused for every call with the same or smaller sizes.
+ * kda_prefill_chunked). The size depends only on the arguments. It includes
+ * the buffers of the chunk-parallel scan when that scan applies to these
+ * sizes (kda_prefill_scan_segments); a smaller workspace that still holds the
+ * plain path's buffers is accepted and runs the plain scan. An allocation of
+ * this size is valid for every call with the same or smaller sizes.
  */
 size_t kda_prefill_workspace_size(int64_t total_tokens, int32_t num_seqs, int32_t H,
+                                  int32_t Dk, int32_t Dv, int32_t chunk_size,
+                                  kda_dtype_t in_dtype);
+
+/*
+ * Segments of the chunk-parallel scan that kda_prefill_chunked (and the _ex
+ * variant) uses for these sizes on the current device, given a workspace of
+ * kda_prefill_workspace_size(...) bytes; 1 = the plain scan.
+ *
+ * The blockwise recurrence is sequential over chunks, and one sequence with
+ * few heads gives it too few (head, 16-column) blocks to fill the device.
+ * Each chunk step is an affine map of the state (the chunk algebra behind the
+ * report's FlashKDA note, "Methodology notes"), so the library then cuts the
+ * sequence into P segments of whole chunks, scans them all at once (once for
+ * the values, once from the identity to get each segment's linear map),
+ * chains the segment end states in fp32 and adds each segment's start-state
+ * term to its outputs. Used only with cu_seqlens == NULL (one sequence), both
+ * phases in one call, no checkpoints and no positions, and only when the
+ * workspace holds the extra buffers (the plain path runs otherwise, with
+ * identical semantics). Host-only query (reads the device's CU count); 0 for
+ * invalid sizes.
+ */
+int32_t kda_prefill_scan_segments(int64_t total_tokens, int32_t num_seqs, int32_t H,
                                   int32_t Dk, int32_t Dv, int32_t chunk_size,
                                   kda_dtype_t in_dtype);
 

@@ -18,6 +18,7 @@ KDA_F32, KDA_BF16 = 0, 1
 
 # Every symbol include/kda.h declares.
 EXPORTS = ("kda_version", "kda_status_string", "kda_prefill_workspace_size",
+           "kda_prefill_scan_segments",
            "kda_prefill_chunked", "kda_prefill_chunked_phases", "kda_prefill_chunked_ex",
            "kda_prefill_chunked_at",
            "kda_decode_step", "kda_decode_step_ex")
@@ -52,6 +53,8 @@ def load():
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_prefill_workspace_size.argtypes = [I64, I32, I32, I32, I32, I32, ctypes.c_int]
     lib.kda_prefill_workspace_size.restype = SZ
+    lib.kda_prefill_scan_segments.argtypes = [I64, I32, I32, I32, I32, I32, ctypes.c_int]
+    lib.kda_prefill_scan_segments.restype = I32
     lib.kda_prefill_chunked.argtypes = [
         P, P, P, ctypes.c_int, P, P, P, I32, I64, I32, I32, I32, I32, P, P, I64, P, I64, P, P,
         SZ, P]
@@ -86,6 +89,11 @@ def workspace_size(total_tokens, num_seqs, H, Dk, Dv, dtype_code, chunk_size=64)
     return int(load().kda_prefill_workspace_size(int(total_tokens), int(num_seqs), int(H),
                                                  int(Dk), int(Dv), int(chunk_size),
                                                  int(dtype_code)))
+
+
+def scan_segments(total_tokens, num_seqs, H, Dk, Dv, dtype_code, chunk_size=64) -> int:
+    return int(load().kda_prefill_scan_segments(int(total_tokens), int(num_seqs), int(H), int(Dk),
+                                                int(Dv), int(chunk_size), int(dtype_code)))
 
 
 def prefill_raw(q, k, v, dtype_code, g, beta, cu_seqlens, num_seqs, total_tokens, H, Dk, Dv,

@@ -50,6 +50,15 @@ def kda_prefill_workspace_size(total_tokens, num_seqs, H, Dk, Dv, dtype=torch.bf
     return B.workspace_size(total_tokens, num_seqs, H, Dk, Dv, code, chunk_size)
 
 
+def kda_prefill_scan_segments(total_tokens, num_seqs, H, Dk, Dv, dtype=torch.bfloat16,
+                              chunk_size=CHUNK) -> int:
+    """Segments of the chunk-parallel scan kda_prefill_chunked uses for these
+    sizes on the current device with a workspace of kda_prefill_workspace_size
+    bytes (1 = plain scan; include/kda.h, kda_prefill_scan_segments)."""
+    code = B.KDA_BF16 if dtype == torch.bfloat16 else B.KDA_F32
+    return B.scan_segments(total_tokens, num_seqs, H, Dk, Dv, code, chunk_size)
+
+
 def kda_prefill_chunked(q, k, v, g, beta, *, cu_seqlens=None, num_seqs=None,
                         initial_state=None, output_final_state=True, final_state=None,
                         ckpt_interval=0, num_checkpoints=None, ckpt_states=None, o=None,

@@ -56,7 +56,24 @@ size_t kda_prefill_workspace_size(int64_t total_tokens, int32_t num_seqs, int32_
                                   int32_t Dv, int32_t chunk_size, kda_dtype_t in_dtype) {
     if (check_prefill_sizes(total_tokens, num_seqs, H, Dk, Dv, chunk_size, in_dtype) != KDA_OK)
         return 0;
-    return kda::prefill_workspace_bytes(total_tokens, num_seqs, H, Dk, Dv, in_dtype == KDA_BF16);
+    const bool bf16 = in_dtype == KDA_BF16;
+    const size_t plain = kda::prefill_workspace_bytes(total_tokens, num_seqs, H, Dk, Dv, bf16);
+    const size_t split = kda::prefill_split_workspace_bytes(total_tokens, num_seqs, H, Dk, Dv, bf16);
+    return plain > split ? plain : split;
+}
+
+int32_t kda_prefill_scan_segments(int64_t total_tokens, int32_t num_seqs, int32_t H, int32_t Dk,
+                                  int32_t Dv, int32_t chunk_size, kda_dtype_t in_dtype) {
+    if (check_prefill_sizes(total_tokens, num_seqs, H, Dk, Dv, chunk_size, in_dtype) != KDA_OK)
+        return 0;
+    int cus = 0, dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 1;
+    const int want = kda::prefill_split_segments(total_tokens, num_seqs, H, Dk, Dv, cus);
+    const int sized = kda::prefill_split_segments(total_tokens, num_seqs, H, Dk, Dv, kda::kSizingCUs);
+    const int P = want < sized ? want : sized;
+    return P < 2 ? 1 : P;
 }
 
 kda_status_t kda_prefill_chunked_at(const void* q, const void* k, const void* v,

@@ -55,10 +55,24 @@ struct PrefillArgs {
     PosArgs pos;
 };
 
-// Bytes of workspace the prefill path needs (0 if unsupported).
+// Bytes of workspace the plain prefill path needs (prep, K1, one scan).
 size_t prefill_workspace_bytes(int64_t total_tokens, int num_seqs, int H, int Dk, int Dv,
                                bool bf16);
 
+// The plain path: prep + K1 and/or one scan over all chunks of each sequence.
+hipError_t launch_prefill_plain(const PrefillArgs& a, hipStream_t stream);
+
+// Chunk-parallel path for one sequence with few heads (kda_split.hip):
+// segments it would cut the sequence into on a device with `cus` CUs (1 = not
+// used), and the workspace it needs when the workspace is sized for
+// kSizingCUs (0 = never used for these sizes).
+constexpr int kSizingCUs = 256;
+int prefill_split_segments(int64_t total_tokens, int num_seqs, int H, int Dk, int Dv, int cus);
+size_t prefill_split_workspace_bytes(int64_t total_tokens, int num_seqs, int H, int Dk, int Dv,
+                                     bool bf16);
+
+// Entry of every prefill call: the chunk-parallel path when it applies and the
+// workspace allows it, else the plain path.
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 
 // Advances each stored chunk-start state of a requested position by the

@@ -2058,7 +2058,7 @@ size_t prefill_workspace_bytes(int64_t total_tokens, int num_seqs, int H, int Dk
            (size_t)H * (size_t)max_chunks(total_tokens, num_seqs) * handoff_bytes(Dk, bf16);
 }
 
-hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
+hipError_t launch_prefill_plain(const PrefillArgs& a, hipStream_t stream) {
     const bool b = a.bf16;
     if (a.Dk == 128 && a.Dv == 128) return b ? launch_typed<128, 128, true>(a, stream) : launch_typed<128, 128, false>(a, stream);
     if (a.Dk == 128 && a.Dv == 64) return b ? launch_typed<128, 64, true>(a, stream) : launch_typed<128, 64, false>(a, stream);

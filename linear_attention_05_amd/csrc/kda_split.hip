@@ -1,0 +1,359 @@
+// kda_split.hip -- chunk-parallel prefill of one sequence with few heads.
+//
+// The blockwise recurrence is sequential over chunks, so one sequence with
+// few heads leaves most CUs idle: its scan has H * Dv / 16 column blocks. The
+// chunk step is affine in the state (from the chunk algebra of the Kimi K3
+// report's FlashKDA note, "Methodology notes"):
+//     S_{n+1} = (Diag(Gamma_last) - Kc^T W) S_n + Kc^T U0,
+// so a segment of chunks maps its start state X to M X + F, and every output
+// row of the segment is o_t = o_t(X = 0) + (M_t^T q_t)^T X, where M_t is the
+// product of the maps up to token t. The sequence is cut into P segments of
+// whole chunks, treated as P independent pseudo-sequences:
+//   1. prepare (K1) once for all segments, then scan A: the value columns with
+//      the true initial state for segment 0 and zeros for the others
+//      -> o(X = 0) into o, end states F_p;
+//   2. scan B on the same handoff: zero values and the identity as initial
+//      state -> end states M_p and outputs oI_t = (M_t^T q_t)^T, Dk columns;
+//   3. combine (fp32, sequential over segments): scan A already started
+//      segment 0 from S_0, so S_end(0) = F_0; for p >= 1 the true start state
+//      is X_p = S_end(p-1) and S_end(p) = M_p X_p + F_p;
+//   4. correct: o_t += oI_t X_p for every token of segments 1 .. P-1 (fp32).
+// Both scans run P * H * D / 16 column blocks at once over chains P times
+// shorter. Everything here is fp32 except the scans themselves, which are the
+// plain path's kernels.
+#include "kda_internal.h"
+
+namespace kda {
+namespace {
+
+constexpr int kT = 256;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+// Upper limit on segments: keeps the sequential combine short.
+constexpr int kMaxSegments = 16;
+// Each segment spans at least this many chunks.
+constexpr int64_t kMinSegmentChunks = 8;
+// Fewer segments than this leave too little gain to pay for the second scan.
+constexpr int kMinSegments = 6;
+
+// Workspace of the split path, after the plain path's workspace for P
+// pseudo-sequences (offsets in bytes, all 256-byte aligned).
+struct SplitLayout {
+    size_t plain, pcu, init_a, fin_a, xst, init_b, fin_b, zero_v, o_i, end;
+};
+
+SplitLayout split_layout(int64_t N, int P, int H, int Dk, int Dv, bool bf16) {
+    SplitLayout L;
+    const size_t st_v = (size_t)P * H * Dk * Dv * sizeof(float);
+    const size_t st_k = (size_t)P * H * Dk * Dk * sizeof(float);
+    L.plain = align256(prefill_workspace_bytes(N, P, H, Dk, Dv, bf16));
+    L.pcu = L.plain;
+    L.init_a = L.pcu + align256((size_t)(P + 1) * sizeof(int32_t));
+    L.fin_a = L.init_a + align256(st_v);
+    L.xst = L.fin_a + align256(st_v);
+    L.init_b = L.xst + align256(st_v);
+    L.fin_b = L.init_b + align256(st_k);
+    L.zero_v = L.fin_b + align256(st_k);
+    L.o_i = L.zero_v + align256((size_t)N * H * Dk * (bf16 ? 2 : 4));
+    L.end = L.o_i + align256((size_t)N * H * Dk * sizeof(float));
+    return L;
+}
+
+// ---------------------------------------------------------------- fill ----
+// Pseudo-sequence boundaries, scan A's initial states (segment 0: the
+// caller's, else zeros), scan B's identity initial states, zero values.
+__global__ __launch_bounds__(kT) void split_fill_kernel(int32_t* __restrict__ pcu, int P,
+                                                        int64_t seg_tokens, int64_t N,
+                                                        const float* __restrict__ s0,
+                                                        float* __restrict__ init_a,
+                                                        float* __restrict__ init_b,
+                                                        f32x4* __restrict__ zero_v, int64_t zero_vec4,
+                                                        int H, int Dk, int Dv) {
+    const int64_t tid = (int64_t)blockIdx.x * kT + threadIdx.x;
+    const int64_t stride = (int64_t)gridDim.x * kT;
+    if (tid <= P) {
+        const int64_t b = tid * seg_tokens;
+        pcu[tid] = (int32_t)(b < N ? b : N);
+    }
+    const int64_t one = (int64_t)H * Dk * Dv;  // states of one pseudo-sequence
+    for (int64_t i = tid; i < (int64_t)P * one; i += stride)
+        init_a[i] = (i < one && s0 != nullptr) ? s0[i] : 0.f;
+    const int64_t sq = (int64_t)Dk * Dk;
+    for (int64_t i = tid; i < (int64_t)P * H * sq; i += stride) {
+        const int64_t e = i % sq;
+        init_b[i] = (e / Dk == e % Dk) ? 1.f : 0.f;
+    }
+    for (int64_t i = tid; i < zero_vec4; i += stride) zero_v[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+// ------------------------------------------------------------- combine ----
+// One workgroup per (head, 16 value columns), sequential over segments:
+//   S_end(0) = F_0;  for p >= 1: X_p = S_end(p-1), S_end(p) = M_p X_p + F_p.
+// X_p (p >= 1) goes to xst for the output correction; S_end(P-1) is the final
+// state. M_p X_p runs on v_mfma_f32_16x16x4_f32 with one wave per 16-row tile
+// of the state (DK / 16 waves). K step (s, e) takes K index 16 s + 4 g + e in
+// lane group g, so each lane reads 16-byte pieces of its M row; X (K x 16
+// columns) sits in LDS. M and F do not depend on the chain: each wave loads
+// them two segments ahead.
+template <int DK>
+__global__ __launch_bounds__(DK * 4) void split_combine_kernel(const float* __restrict__ fin_a,
+                                                               const float* __restrict__ fin_b,
+                                                               float* __restrict__ xst,
+                                                               float* __restrict__ final_state,
+                                                               int P, int H, int Dv) {
+    constexpr int NT = DK * 4;  // threads
+    constexpr int KS = DK / 16;  // 16-byte pieces per M row
+    __shared__ float sX[DK][16 + 1];
+    const int h = blockIdx.x, j0 = blockIdx.y * 16;
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int m = lane & 15, q = lane >> 4;
+    const size_t sv = (size_t)DK * Dv, sk = (size_t)DK * DK;
+    struct Step {
+        f32x4 A[KS];
+        f32x4 F;
+    };
+    auto load_step = [&](int p, Step& st) {
+        if (p >= P) return;
+        const float* M = fin_b + ((size_t)p * H + h) * sk + (size_t)(16 * wave + m) * DK + 4 * q;
+        const float* Fp = fin_a + ((size_t)p * H + h) * sv + (size_t)(16 * wave + 4 * q) * Dv + j0 + m;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) st.A[s] = *reinterpret_cast<const f32x4*>(M + 16 * s);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) st.F[i] = Fp[(size_t)i * Dv];
+    };
+    // S_end(0) = F_0
+    for (int i = t; i < DK * 16; i += NT) sX[i / 16][i % 16] = fin_a[((size_t)h * DK + i / 16) * Dv + j0 + i % 16];
+    Step cur, nxt;
+    load_step(1, cur);
+    load_step(2, nxt);
+    __syncthreads();
+    for (int p = 1; p < P; ++p) {
+        // X_p = S_end(p-1)
+        float* X = xst + ((size_t)p * H + h) * sv;
+        for (int i = t; i < DK * 16; i += NT) X[(size_t)(i / 16) * Dv + j0 + i % 16] = sX[i / 16][i % 16];
+        Step far;
+        load_step(p + 2, far);
+        // four independent accumulation chains (K steps e = 0..3), summed at the end
+        f32x4 acc[4] = {cur.F, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                acc[e] = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.A[s][e], sX[16 * s + 4 * q + e][m], acc[e], 0, 0, 0);
+        const f32x4 res = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+        __syncthreads();  // every wave has read X_p
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sX[16 * wave + 4 * q + i][m] = res[i];
+        __syncthreads();
+        cur = nxt;
+        nxt = far;
+    }
+    if (final_state != nullptr)
+        for (int i = t; i < DK * 16; i += NT)
+            final_state[((size_t)h * DK + i / 16) * Dv + j0 + i % 16] = sX[i / 16][i % 16];
+}
+
+// ---------------------------------------------------------- correction ----
+// o_t += oI_t X_p for the tokens of segments 1 .. P-1, as the transposed
+// product (o_corr)^T = X_p^T oI^T on v_mfma_f32_16x16x4_f32, so that each
+// lane's result is four consecutive value columns of one token (16-byte
+// read-modify-write of o). One workgroup per (head, segment, group of up to
+// kMaxGroup chunks inside the segment); wave w owns value-column tiles w + 4 j.
+// The A operands (X_p^T rows) stay in registers for the whole group; B
+// operands are 16-byte pieces of oI rows, K step (s, e) taking K index
+// 16 s + 4 g + e in lane group g. The oI rows and the old o values of the
+// next 16-token tile are loaded while the current one is multiplied.
+constexpr int kMaxGroup = 8;
+
+template <int DK, int DV>
+__global__ __launch_bounds__(kT) void split_correct_kernel(const float* __restrict__ o_i,
+                                                           const float* __restrict__ xst,
+                                                           float* __restrict__ o, int64_t N, int H,
+                                                           int64_t seg_chunks, int64_t groups_per_seg,
+                                                           int group) {
+    constexpr int CTW = DV / 64;  // column tiles per wave
+    constexpr int KS = DK / 16;
+    const int h = (int)(blockIdx.x % (unsigned)H);
+    const int64_t wg = (int64_t)(blockIdx.x / (unsigned)H);
+    const int p = 1 + (int)(wg / groups_per_seg);
+    const int64_t nchunks = (N + 63) / 64;
+    const int64_t c0 = p * seg_chunks + (wg % groups_per_seg) * group;
+    int64_t c1 = c0 + group;
+    c1 = c1 < (p + 1) * seg_chunks ? c1 : (p + 1) * seg_chunks;
+    c1 = c1 < nchunks ? c1 : nchunks;
+    if (c0 >= c1) return;  // uniform over the workgroup
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int m = lane & 15, q = lane >> 4;
+    f32x4 XA[CTW][KS];  // X_p^T[16 ct + m][16 s + 4 q + e] = X_p[16 s + 4 q + e][16 ct + m]
+    {
+        const float* X = xst + ((size_t)p * H + h) * DK * DV;
+#pragma unroll
+        for (int j = 0; j < CTW; ++j)
+#pragma unroll
+            for (int s = 0; s < KS; ++s)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    XA[j][s][e] = X[(size_t)(16 * s + 4 * q + e) * DV + 16 * (wave + 4 * j) + m];
+    }
+    struct Tile {
+        f32x4 B[KS];
+        f32x4 old[CTW];
+    };
+    const int nt = (int)(c1 - c0) * 4;  // 16-token tiles
+    auto tok_of = [&](int u) { return c0 * 64 + 16 * u + m; };
+    auto load_tile = [&](int u, Tile& tl) {
+        const int64_t tok = tok_of(u);
+        const bool ok = tok < N;
+        const int64_t row = (ok ? tok : 0) * H + h;
+        const float* src = o_i + row * (int64_t)DK + 4 * q;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            const f32x4 v = *reinterpret_cast<const f32x4*>(src + 16 * s);
+            tl.B[s] = ok ? v : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        const float* dst = o + row * (int64_t)DV + 4 * q;
+#pragma unroll
+        for (int j = 0; j < CTW; ++j) tl.old[j] = *reinterpret_cast<const f32x4*>(dst + 16 * (wave + 4 * j));
+    };
+    Tile cur;
+    load_tile(0, cur);
+    for (int u = 0; u < nt; ++u) {
+        Tile nxt;
+        if (u + 1 < nt) load_tile(u + 1, nxt);
+        const int64_t tok = tok_of(u);
+        // independent chains: every column tile, and K steps e < 2 / e >= 2
+        f32x4 acc[CTW][2];
+#pragma unroll
+        for (int j = 0; j < CTW; ++j) {
+            acc[j][0] = cur.old[j];
+            acc[j][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+                for (int j = 0; j < CTW; ++j)
+                    acc[j][e >> 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(XA[j][s][e], cur.B[s][e], acc[j][e >> 1], 0, 0, 0);
+        if (tok < N)
+#pragma unroll
+            for (int j = 0; j < CTW; ++j)
+                *reinterpret_cast<f32x4*>(o + (tok * H + h) * (int64_t)DV + 16 * (wave + 4 * j) + 4 * q) = acc[j][0] + acc[j][1];
+        cur = nxt;
+    }
+}
+
+template <int DK, int DV>
+hipError_t launch_fix(const float* fin_a, const float* fin_b, float* xst, float* final_state,
+                      const float* o_i, float* o, int64_t N, int H, int P, int64_t seg_chunks,
+                      hipStream_t stream) {
+    hipLaunchKernelGGL((split_combine_kernel<DK>), dim3((unsigned)H, DV / 16), dim3(DK * 4), 0,
+                       stream, fin_a, fin_b, xst, final_state, P, H, DV);
+    // chunks per workgroup: up to kMaxGroup, fewer when that leaves under
+    // about four workgroups per CU
+    const int64_t fix_chunks = (int64_t)(P - 1) * seg_chunks * H;
+    int64_t group = fix_chunks / (4 * kSizingCUs);
+    group = group < 1 ? 1 : (group > kMaxGroup ? kMaxGroup : group);
+    const int64_t groups_per_seg = (seg_chunks + group - 1) / group;
+    const int64_t wgs = (int64_t)(P - 1) * groups_per_seg * H;
+    if (wgs > 0)
+        hipLaunchKernelGGL((split_correct_kernel<DK, DV>), dim3((unsigned)wgs), dim3(kT), 0, stream,
+                           o_i, xst, o, N, H, seg_chunks, groups_per_seg, (int)group);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+int prefill_split_segments(int64_t total_tokens, int num_seqs, int H, int Dk, int Dv, int cus) {
+    if (num_seqs != 1 || total_tokens <= 0 || cus <= 0) return 1;
+    const int64_t nchunks = (total_tokens + 63) / 64;
+    const int64_t blocks = (int64_t)H * ((Dk > Dv ? Dk : Dv) / 16);  // wider scan's workgroups
+    int64_t P = cus / blocks;
+    P = P < nchunks / kMinSegmentChunks ? P : nchunks / kMinSegmentChunks;
+    P = P < kMaxSegments ? P : kMaxSegments;
+    // two scans of 1/P of the chain plus the combine and the correction: measured
+    // on MI355X (D = 128, T = 65536) 3.0x faster than the plain scan at P = 16,
+    // 1.6x at P = 8, 1.03x at P = 4
+    if (P < kMinSegments) return 1;
+    const int64_t seg = (nchunks + P - 1) / P;
+    return (int)((nchunks + seg - 1) / seg);
+}
+
+size_t prefill_split_workspace_bytes(int64_t total_tokens, int num_seqs, int H, int Dk, int Dv,
+                                     bool bf16) {
+    const int P = prefill_split_segments(total_tokens, num_seqs, H, Dk, Dv, kSizingCUs);
+    if (P < 2) return 0;
+    return split_layout(total_tokens, P, H, Dk, Dv, bf16).end;
+}
+
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
+    const bool eligible = a.cu_seqlens == nullptr && a.num_seqs == 1 && a.phases == 3u &&
+                          a.ckpt_interval == 0 && a.pos.num_pos == 0 && a.total_tokens > 0;
+    int P = 1;
+    if (eligible) {
+        int cus = 0, dev = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess) {
+            const int want = prefill_split_segments(a.total_tokens, 1, a.H, a.Dk, a.Dv, cus);
+            const int sized = prefill_split_segments(a.total_tokens, 1, a.H, a.Dk, a.Dv, kSizingCUs);
+            // the workspace was sized for `sized` segments: never use more
+            P = want < sized ? want : sized;
+            if (P >= 2 && split_layout(a.total_tokens, P, a.H, a.Dk, a.Dv, a.bf16).end > a.workspace_bytes)
+                P = 1;
+        }
+    }
+    if (P < 2) return launch_prefill_plain(a, stream);
+
+    const int64_t N = a.total_tokens;
+    const int64_t nchunks = (N + 63) / 64;
+    const int64_t seg_chunks = (nchunks + P - 1) / P;
+    const SplitLayout L = split_layout(N, P, a.H, a.Dk, a.Dv, a.bf16);
+    unsigned char* ws = static_cast<unsigned char*>(a.workspace);
+    int32_t* pcu = reinterpret_cast<int32_t*>(ws + L.pcu);
+    float* init_a = reinterpret_cast<float*>(ws + L.init_a);
+    float* fin_a = reinterpret_cast<float*>(ws + L.fin_a);
+    float* xst = reinterpret_cast<float*>(ws + L.xst);
+    float* init_b = reinterpret_cast<float*>(ws + L.init_b);
+    float* fin_b = reinterpret_cast<float*>(ws + L.fin_b);
+    void* zero_v = ws + L.zero_v;
+    float* o_i = reinterpret_cast<float*>(ws + L.o_i);
+
+    const int64_t zero_vec4 = N * a.H * a.Dk * (a.bf16 ? 2 : 4) / 16;
+    {
+        const int64_t work = (int64_t)P * a.H * a.Dk * (a.Dk > a.Dv ? a.Dk : a.Dv);
+        const int64_t most = work > zero_vec4 ? work : zero_vec4;
+        int64_t blocks = (most + kT - 1) / kT;
+        blocks = blocks < 4096 ? blocks : 4096;
+        hipLaunchKernelGGL(split_fill_kernel, dim3((unsigned)blocks), dim3(kT), 0, stream, pcu, P,
+                           seg_chunks * 64, N, a.initial_state, init_a, init_b,
+                           static_cast<f32x4*>(zero_v), zero_vec4, a.H, a.Dk, a.Dv);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    PrefillArgs A = a;  // scan A: value columns, end states F_p, outputs o(X = 0)
+    A.cu_seqlens = pcu;
+    A.num_seqs = P;
+    A.initial_state = init_a;
+    A.final_state = fin_a;
+    A.workspace_bytes = L.plain;
+    hipError_t e = launch_prefill_plain(A, stream);
+    if (e != hipSuccess) return e;
+    PrefillArgs Bs = A;  // scan B: zero values from the identity -> M_p, oI
+    Bs.v = zero_v;
+    Bs.Dv = a.Dk;
+    Bs.initial_state = init_b;
+    Bs.final_state = fin_b;
+    Bs.o = o_i;
+    Bs.phases = 2u;
+    e = launch_prefill_plain(Bs, stream);
+    if (e != hipSuccess) return e;
+    if (a.Dk == 128 && a.Dv == 128) return launch_fix<128, 128>(fin_a, fin_b, xst, a.final_state, o_i, a.o, N, a.H, P, seg_chunks, stream);
+    if (a.Dk == 128 && a.Dv == 64) return launch_fix<128, 64>(fin_a, fin_b, xst, a.final_state, o_i, a.o, N, a.H, P, seg_chunks, stream);
+    if (a.Dk == 64 && a.Dv == 128) return launch_fix<64, 128>(fin_a, fin_b, xst, a.final_state, o_i, a.o, N, a.H, P, seg_chunks, stream);
+    if (a.Dk == 64 && a.Dv == 64) return launch_fix<64, 64>(fin_a, fin_b, xst, a.final_state, o_i, a.o, N, a.H, P, seg_chunks, stream);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace kda

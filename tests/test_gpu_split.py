@@ -1,0 +1,96 @@
+"""GPU parity of the chunk-parallel scan (one sequence, few heads) against the
+fp64 oracle, through the C ABI.
+
+kda_prefill_chunked cuts such a sequence into segments of whole chunks,
+scans them at once (values, and the identity for each segment's linear map),
+chains the segment end states and corrects the outputs. The same inputs run
+through the plain path (prepare and scan as two calls) must agree with the
+oracle too."""
+
+import numpy as np
+import pytest
+
+from helpers import assert_parity, dev_tensor
+from oracle import recurrence
+from synth import make_prefill
+
+pytestmark = pytest.mark.gpu
+
+CASES = [  # H, Dk, Dv, dtype, T, initial state
+    (4, 128, 128, "bf16", 8192, True),
+    (1, 128, 128, "bf16", 4133, True),
+    (5, 128, 64, "bf16", 3072, True),
+    (3, 64, 128, "bf16", 5000, False),
+    (2, 64, 64, "f32", 4000, False),
+    (2, 128, 128, "f32", 3300, True),
+]
+
+
+def run(x, *, phases=None, final=True):
+    import torch
+    import linear_attention_05_amd as K
+    from linear_attention_05_amd import _binding as B
+    q, k, v, g, beta = (dev_tensor(a) for a in (x.q, x.k, x.v, x.g, x.beta))
+    s0 = dev_tensor(x.initial_state) if x.initial_state is not None else None
+    if phases is None:
+        o, fs, _ = K.kda_prefill_chunked(q, k, v, g, beta, initial_state=s0,
+                                         output_final_state=final)
+    else:  # prepare and scan as two calls: always the plain scan
+        ws = torch.empty(K.kda_prefill_workspace_size(x.total_tokens, 1, x.H, x.Dk, x.Dv, q.dtype),
+                         dtype=torch.uint8, device=q.device)
+        o = torch.empty(x.total_tokens, x.H, x.Dv, device=q.device)
+        fs = torch.empty(1, x.H, x.Dk, x.Dv, device=q.device)
+        for p in (B.PHASE_PREPARE, B.PHASE_SCAN):
+            K.kda_prefill_chunked(q, k, v, g, beta, initial_state=s0, final_state=fs, o=o,
+                                  workspace=ws, phases=p)
+    torch.cuda.synchronize()
+    return o.cpu().numpy(), (None if fs is None else fs.cpu().numpy())
+
+
+def segments(x):
+    import torch
+    import linear_attention_05_amd as K
+    dt = torch.bfloat16 if x.dtype == "bf16" else torch.float32
+    return K.kda_prefill_scan_segments(x.total_tokens, 1, x.H, x.Dk, x.Dv, dt)
+
+
+@pytest.mark.parametrize("H,Dk,Dv,dtype,T,init", CASES)
+def test_split_matches_oracle(H, Dk, Dv, dtype, T, init):
+    x = make_prefill([T], H, Dk, Dv, dtype, 700 + T % 97 + H, init_state=init)
+    P = segments(x)
+    print(f"split prefill H={H} Dk={Dk} Dv={Dv} {dtype} T={T} init={init}: {P} segments",
+          flush=True)
+    assert P >= 6, "these sizes should take the chunk-parallel scan"
+    r = recurrence.prefill(x.q, x.k, x.v, x.g, x.beta, x.cu_seqlens,
+                           initial_state=x.initial_state)
+    o, fs = run(x)
+    assert_parity(o, r["o"], dtype, "split o")
+    assert_parity(fs, r["final"], dtype, "split final state")
+    o2, fs2 = run(x, phases="split calls")
+    assert_parity(o2, r["o"], dtype, "plain o")
+    assert_parity(fs2, r["final"], dtype, "plain final state")
+
+
+def test_split_without_final_state():
+    x = make_prefill([3100], 2, 128, 128, "bf16", 771, init_state=True)
+    assert segments(x) >= 6
+    o, fs = run(x, final=False)
+    assert fs is None
+    r = recurrence.prefill(x.q, x.k, x.v, x.g, x.beta, x.cu_seqlens,
+                           initial_state=x.initial_state)
+    assert_parity(o, r["o"], "bf16", "split o, no final state")
+
+
+def test_segment_rule():
+    """The headline shape (32 heads) fills the device with the plain scan;
+    short sequences and varlen batches never split."""
+    import torch
+    import linear_attention_05_amd as K
+    bf = torch.bfloat16
+    assert K.kda_prefill_scan_segments(8192, 1, 32, 128, 128, bf) == 1
+    assert K.kda_prefill_scan_segments(1024, 1, 1, 128, 128, bf) == 1
+    assert K.kda_prefill_scan_segments(8192, 2, 1, 128, 128, bf) == 1
+    assert K.kda_prefill_scan_segments(8192, 1, 4, 128, 128, bf) == 8
+    assert K.kda_prefill_scan_segments(65536, 1, 8, 128, 128, bf) == 1
+    assert K.kda_prefill_scan_segments(65536, 1, 1, 128, 128, bf) == 16
+    assert K.kda_prefill_scan_segments(8192, 1, 1, 128, 128, bf, chunk_size=32) == 0
