@@ -141,3 +141,29 @@ def test_decode_batch_rows_independent():
     assert np.array_equal(o2[4, 1], o[4, 1])
     assert np.array_equal(part[4, 1], full[4, 1])
     assert np.array_equal(part[0], s0[0])
+
+
+@pytest.mark.parametrize("cut", [1, 40, 64, 129])
+def test_segment_affine_decomposition(cut):
+    """The chunk-parallel scan's decomposition, on the recurrence itself: a
+    segment started from state X gives o = o(X = 0) + oI X and S_end = M X + F,
+    where (oI, M) are the outputs and end state of the same segment run with
+    zero values from the identity, and (o(X = 0), F) the run from zeros."""
+    x = make_prefill([200], 2, 8, 6, "f32", 24, init_state=True)
+    T, H, Dk, Dv = 200, 2, 8, 6
+    full = recurrence.prefill(x.q, x.k, x.v, x.g, x.beta, x.cu_seqlens,
+                              initial_state=x.initial_state)
+    head = recurrence.prefill(x.q[:cut], x.k[:cut], x.v[:cut], x.g[:cut], x.beta[:cut],
+                              np.array([0, cut]), initial_state=x.initial_state)
+    X = head["final"][0]  # [H, Dk, Dv], the true start state of the tail segment
+    tail = (x.q[cut:], x.k[cut:], x.v[cut:], x.g[cut:], x.beta[cut:])
+    cu = np.array([0, T - cut])
+    a = recurrence.prefill(*tail, cu)
+    eye = np.broadcast_to(np.eye(Dk, dtype=np.float32), (1, H, Dk, Dk)).copy()
+    zero_v = np.zeros((T - cut, H, Dk), dtype=np.float32)
+    b = recurrence.prefill(tail[0], tail[1], zero_v, tail[3], tail[4], cu, initial_state=eye)
+    o_rec = a["o"] + np.einsum("thk,hkv->thv", b["o"], X)
+    s_rec = np.einsum("hij,hjv->hiv", b["final"][0], X) + a["final"][0]
+    assert _max_rel(o_rec, full["o"][cut:]) < 1e-12
+    assert _max_rel(s_rec, full["final"][0]) < 1e-12
+    assert _max_rel(head["o"], full["o"][:cut]) == 0.0
