@@ -29,10 +29,14 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 MFMA_FILE = os.path.join(ROOT, "profiles", "mfma.json")
 
 
+# Sources of the kernels whose counters profiles/ holds (K1, the scans, decode).
+MEASURED_SOURCES = ("kda_internal.h", "kda_prefill.hip", "kda_decode.hip")
+
+
 def kernel_source_sha() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "linear_attention_05_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in MEASURED_SOURCES:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -475,7 +479,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--decode-steps", type=int, default=64)
-    ap.add_argument("--only", choices=["all", "prefill", "decode"], default="all")
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "few_heads"], default="all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra-workloads", action="store_true",
                     help="skip timing the long-context and varlen prefill workloads")
@@ -519,6 +523,11 @@ def main():
         del a, b
 
     out = {}
+    if args.only == "few_heads":
+        out["few_heads"] = [bench_few_heads(4), bench_few_heads(1)]
+        out["kernel_source_sha"] = kernel_source_sha()
+        print(json.dumps(out), flush=True)
+        return
     if args.only in ("all", "prefill"):
         p = bench_prefill(args.steps, args.warmup)
         step_ms = p["wall_ms"]
