@@ -157,15 +157,21 @@ __global__ __launch_bounds__(DK * 4) void split_combine_kernel(const float* __re
 
 // ---------------------------------------------------------- correction ----
 // o_t += oI_t X_p for the tokens of segments 1 .. P-1, as the transposed
-// product (o_corr)^T = X_p^T oI^T on v_mfma_f32_16x16x4_f32, so that each
-// lane's result is four consecutive value columns of one token (16-byte
-// read-modify-write of o). One workgroup per (head, segment, group of up to
-// kMaxGroup chunks inside the segment); wave w owns value-column tiles w + 4 j.
-// The A operands (X_p^T rows) stay in registers for the whole group; B
-// operands are 16-byte pieces of oI rows, K step (s, e) taking K index
-// 16 s + 4 g + e in lane group g. The oI rows and the old o values of the
-// next 16-token tile are loaded while the current one is multiplied.
+// product (o_corr)^T = X_p^T oI^T, so that each lane's result is four
+// consecutive value columns of one token (16-byte read-modify-write of o).
+// Both operands are split into fp16 pairs x = hi + lo and the product takes
+// three passes of v_mfma_f32_16x16x32_f16 (hi hi, hi lo, lo hi) with fp32
+// accumulation: the dropped lo lo term is about 2^-22 of each product, so the
+// correction keeps fp32 accuracy at three times the fp16 rate instead of the
+// fp32 matrix-core rate (8x lower). One workgroup per (head, segment, group of
+// up to kMaxGroup chunks inside the segment); wave w owns value-column tiles
+// w + 4 j, whose X_p^T operand pairs stay in registers for the whole group.
+// Fragments: lane l holds row (A) or column (B) l % 16 at K = 8 (l / 16) + e.
 constexpr int kMaxGroup = 8;
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ _Float16 f16_hi(float x) { return (_Float16)x; }
+__device__ __forceinline__ _Float16 f16_lo(float x) { return (_Float16)(x - (float)(_Float16)x); }
 
 template <int DK, int DV>
 __global__ __launch_bounds__(kT) void split_correct_kernel(const float* __restrict__ o_i,
@@ -174,7 +180,7 @@ __global__ __launch_bounds__(kT) void split_correct_kernel(const float* __restri
                                                            int64_t seg_chunks, int64_t groups_per_seg,
                                                            int group) {
     constexpr int CTW = DV / 64;  // column tiles per wave
-    constexpr int KS = DK / 16;
+    constexpr int KS = DK / 32;   // 32-wide K steps
     const int h = (int)(blockIdx.x % (unsigned)H);
     const int64_t wg = (int64_t)(blockIdx.x / (unsigned)H);
     const int p = 1 + (int)(wg / groups_per_seg);
@@ -186,62 +192,62 @@ __global__ __launch_bounds__(kT) void split_correct_kernel(const float* __restri
     if (c0 >= c1) return;  // uniform over the workgroup
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int m = lane & 15, q = lane >> 4;
-    f32x4 XA[CTW][KS];  // X_p^T[16 ct + m][16 s + 4 q + e] = X_p[16 s + 4 q + e][16 ct + m]
+    // A = X_p^T: row 16 ct + m, K = 32 ks + 8 q + e
+    half8 ahi[CTW][KS], alo[CTW][KS];
     {
         const float* X = xst + ((size_t)p * H + h) * DK * DV;
 #pragma unroll
         for (int j = 0; j < CTW; ++j)
 #pragma unroll
-            for (int s = 0; s < KS; ++s)
+            for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    XA[j][s][e] = X[(size_t)(16 * s + 4 * q + e) * DV + 16 * (wave + 4 * j) + m];
+                for (int e = 0; e < 8; ++e) {
+                    const float x = X[(size_t)(32 * ks + 8 * q + e) * DV + 16 * (wave + 4 * j) + m];
+                    ahi[j][ks][e] = f16_hi(x);
+                    alo[j][ks][e] = f16_lo(x);
+                }
     }
-    struct Tile {
-        f32x4 B[KS];
-        f32x4 old[CTW];
-    };
     const int nt = (int)(c1 - c0) * 4;  // 16-token tiles
-    auto tok_of = [&](int u) { return c0 * 64 + 16 * u + m; };
-    auto load_tile = [&](int u, Tile& tl) {
-        const int64_t tok = tok_of(u);
+    for (int u = 0; u < nt; ++u) {
+        const int64_t tok = c0 * 64 + 16 * u + m;
         const bool ok = tok < N;
         const int64_t row = (ok ? tok : 0) * H + h;
-        const float* src = o_i + row * (int64_t)DK + 4 * q;
+        // B = oI^T: column = token 16 u + m, K = 32 ks + 8 q + e
+        half8 bhi[KS], blo[KS];
+        const float* src = o_i + row * (int64_t)DK + 8 * q;
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            const f32x4 v = *reinterpret_cast<const f32x4*>(src + 16 * s);
-            tl.B[s] = ok ? v : f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int ks = 0; ks < KS; ++ks) {
+            const f32x4 v0 = *reinterpret_cast<const f32x4*>(src + 32 * ks);
+            const f32x4 v1 = *reinterpret_cast<const f32x4*>(src + 32 * ks + 4);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float x = ok ? (e < 4 ? v0[e] : v1[e - 4]) : 0.f;
+                bhi[ks][e] = f16_hi(x);
+                blo[ks][e] = f16_lo(x);
+            }
         }
-        const float* dst = o + row * (int64_t)DV + 4 * q;
+        float* dst = o + row * (int64_t)DV + 4 * q;
+        f32x4 old[CTW];
 #pragma unroll
-        for (int j = 0; j < CTW; ++j) tl.old[j] = *reinterpret_cast<const f32x4*>(dst + 16 * (wave + 4 * j));
-    };
-    Tile cur;
-    load_tile(0, cur);
-    for (int u = 0; u < nt; ++u) {
-        Tile nxt;
-        if (u + 1 < nt) load_tile(u + 1, nxt);
-        const int64_t tok = tok_of(u);
-        // independent chains: every column tile, and K steps e < 2 / e >= 2
+        for (int j = 0; j < CTW; ++j) old[j] = *reinterpret_cast<const f32x4*>(dst + 16 * (wave + 4 * j));
         f32x4 acc[CTW][2];
 #pragma unroll
         for (int j = 0; j < CTW; ++j) {
-            acc[j][0] = cur.old[j];
+            acc[j][0] = old[j];
             acc[j][1] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
 #pragma unroll
-        for (int s = 0; s < KS; ++s)
+        for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-#pragma unroll
-                for (int j = 0; j < CTW; ++j)
-                    acc[j][e >> 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(XA[j][s][e], cur.B[s][e], acc[j][e >> 1], 0, 0, 0);
-        if (tok < N)
+            for (int j = 0; j < CTW; ++j) {
+                acc[j][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[j][ks], bhi[ks], acc[j][0], 0, 0, 0);
+                acc[j][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[j][ks], blo[ks], acc[j][1], 0, 0, 0);
+                acc[j][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[j][ks], bhi[ks], acc[j][1], 0, 0, 0);
+            }
+        if (ok)
 #pragma unroll
             for (int j = 0; j < CTW; ++j)
-                *reinterpret_cast<f32x4*>(o + (tok * H + h) * (int64_t)DV + 16 * (wave + 4 * j) + 4 * q) = acc[j][0] + acc[j][1];
-        cur = nxt;
+                *reinterpret_cast<f32x4*>(dst + 16 * (wave + 4 * j)) = acc[j][0] + acc[j][1];
     }
 }
 
