@@ -103,9 +103,15 @@ __global__ __launch_bounds__(DK * 4) void split_combine_kernel(const float* __re
                                                                float* __restrict__ xst,
                                                                float* __restrict__ final_state,
                                                                int P, int H, int Dv) {
-    constexpr int NT = DK * 4;  // threads
+    constexpr int NT = DK * 4;   // threads
     constexpr int KS = DK / 16;  // 16-byte pieces per M row
-    __shared__ float sX[DK][16 + 1];
+    constexpr int XP = DK + 4;   // padded LDS row of X^T
+    // X_p^T for every segment (column c of the block is row c here, so a
+    // lane's four K values of a K step are one 16-byte read and its four
+    // result rows one 16-byte write). Slot p holds X_p (slot P: the final
+    // state); the chain stores nothing to global memory until it is done,
+    // so its waits on the operand loads never wait for stores as well.
+    __shared__ __attribute__((aligned(16))) float sXs[kMaxSegments + 1][16][XP];
     const int h = blockIdx.x, j0 = blockIdx.y * 16;
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int m = lane & 15, q = lane >> 4;
@@ -123,36 +129,46 @@ __global__ __launch_bounds__(DK * 4) void split_combine_kernel(const float* __re
 #pragma unroll
         for (int i = 0; i < 4; ++i) st.F[i] = Fp[(size_t)i * Dv];
     };
-    // S_end(0) = F_0
-    for (int i = t; i < DK * 16; i += NT) sX[i / 16][i % 16] = fin_a[((size_t)h * DK + i / 16) * Dv + j0 + i % 16];
-    Step cur, nxt;
-    load_step(1, cur);
-    load_step(2, nxt);
+    // X_1 = S_end(0) = F_0
+    for (int i = t; i < DK * 16; i += NT) sXs[1][i % 16][i / 16] = fin_a[((size_t)h * DK + i / 16) * Dv + j0 + i % 16];
+    // Step p uses buffer p % NB; the loads for step p + NB - 1 go into the
+    // buffer step p - 1 has finished with. The loop is unrolled over the largest
+    // segment count with a uniform guard per step, so every buffer index is a
+    // constant and no register holding a load in flight is copied or waited
+    // on before its step (a loop back-edge would wait for every load).
+    constexpr int NB = 4;  // operand buffers: loads run NB - 1 steps ahead
+    Step buf[NB];
+#pragma unroll
+    for (int p = 1; p < NB; ++p) load_step(p, buf[p % NB]);
     __syncthreads();
-    for (int p = 1; p < P; ++p) {
-        // X_p = S_end(p-1)
-        float* X = xst + ((size_t)p * H + h) * sv;
-        for (int i = t; i < DK * 16; i += NT) X[(size_t)(i / 16) * Dv + j0 + i % 16] = sX[i / 16][i % 16];
-        Step far;
-        load_step(p + 2, far);
+#pragma unroll
+    for (int p = 1; p < kMaxSegments; ++p) {
+        if (p >= P) continue;
+        load_step(p + NB - 1, buf[(p + NB - 1) % NB]);
+        const Step& cur = buf[p % NB];
+        f32x4 b[KS];  // X_p[16 s + 4 q + e][m]
+#pragma unroll
+        for (int s = 0; s < KS; ++s) b[s] = *reinterpret_cast<const f32x4*>(&sXs[p][m][16 * s + 4 * q]);
         // four independent accumulation chains (K steps e = 0..3), summed at the end
         f32x4 acc[4] = {cur.F, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
         for (int s = 0; s < KS; ++s)
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                acc[e] = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.A[s][e], sX[16 * s + 4 * q + e][m], acc[e], 0, 0, 0);
-        const f32x4 res = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-        __syncthreads();  // every wave has read X_p
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sX[16 * wave + 4 * q + i][m] = res[i];
+                acc[e] = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.A[s][e], b[s][e], acc[e], 0, 0, 0);
+        // S_end(p) = X_{p+1}: rows 16 wave + 4 q + i, column m
+        *reinterpret_cast<f32x4*>(&sXs[p + 1][m][16 * wave + 4 * q]) = (acc[0] + acc[1]) + (acc[2] + acc[3]);
         __syncthreads();
-        cur = nxt;
-        nxt = far;
     }
-    if (final_state != nullptr)
-        for (int i = t; i < DK * 16; i += NT)
-            final_state[((size_t)h * DK + i / 16) * Dv + j0 + i % 16] = sX[i / 16][i % 16];
+    // X_p (p = 1 .. P-1) for the output correction, X_P = S_end(P-1) is the final state
+    for (int p = 1; p <= P; ++p) {
+        float* dst = p < P ? xst + ((size_t)p * H + h) * sv : final_state;
+        if (p == P) {
+            if (final_state == nullptr) break;
+            dst += (size_t)h * sv;
+        }
+        for (int i = t; i < DK * 16; i += NT) dst[(size_t)(i / 16) * Dv + j0 + i % 16] = sXs[p][i % 16][i / 16];
+    }
 }
 
 // ---------------------------------------------------------- correction ----
