@@ -477,7 +477,9 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # the GPU reaches its steady clock after about 20 ms of prefill calls (~60
+    # calls at the headline shape): the default warm-up covers that
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--decode-steps", type=int, default=64)
     ap.add_argument("--only", choices=["all", "prefill", "decode", "few_heads"], default="all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -548,6 +550,7 @@ def main():
                        "heads": p["H"], "head_dim": p["D"], "chunk": 64},
             "roofline": dominant,
             "prefill": {
+                "event_ms_per_step": round(p["event_ms"], 4),
                 "tflops_algorithmic": round(p["flops"] / (step_ms * 1e-3) / 1e12, 2),
                 "flops_per_step": p["flops"],
                 "path_compulsory_bytes": p["compulsory_bytes"],
