@@ -97,12 +97,12 @@ __global__ __launch_bounds__(kT) void split_fill_kernel(int32_t* __restrict__ pc
 // lane group g, so each lane reads 16-byte pieces of its M row; X (K x 16
 // columns) sits in LDS. M and F do not depend on the chain: each wave loads
 // them two segments ahead.
-template <int DK>
+template <int DK, int P>
 __global__ __launch_bounds__(DK * 4) void split_combine_kernel(const float* __restrict__ fin_a,
                                                                const float* __restrict__ fin_b,
                                                                float* __restrict__ xst,
                                                                float* __restrict__ final_state,
-                                                               int P, int H, int Dv) {
+                                                               int H, int Dv) {
     constexpr int NT = DK * 4;   // threads
     constexpr int KS = DK / 16;  // 16-byte pieces per M row
     constexpr int XP = DK + 4;   // padded LDS row of X^T
@@ -111,7 +111,7 @@ __global__ __launch_bounds__(DK * 4) void split_combine_kernel(const float* __re
     // result rows one 16-byte write). Slot p holds X_p (slot P: the final
     // state); the chain stores nothing to global memory until it is done,
     // so its waits on the operand loads never wait for stores as well.
-    __shared__ __attribute__((aligned(16))) float sXs[kMaxSegments + 1][16][XP];
+    __shared__ __attribute__((aligned(16))) float sXs[P + 1][16][XP];
     const int h = blockIdx.x, j0 = blockIdx.y * 16;
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int m = lane & 15, q = lane >> 4;
@@ -132,18 +132,17 @@ __global__ __launch_bounds__(DK * 4) void split_combine_kernel(const float* __re
     // X_1 = S_end(0) = F_0
     for (int i = t; i < DK * 16; i += NT) sXs[1][i % 16][i / 16] = fin_a[((size_t)h * DK + i / 16) * Dv + j0 + i % 16];
     // Step p uses buffer p % NB; the loads for step p + NB - 1 go into the
-    // buffer step p - 1 has finished with. The loop is unrolled over the largest
-    // segment count with a uniform guard per step, so every buffer index is a
-    // constant and no register holding a load in flight is copied or waited
-    // on before its step (a loop back-edge would wait for every load).
+    // buffer step p - 1 has finished with. The segment count is a template
+    // parameter and the loop fully unrolled: every buffer index is a constant
+    // and, with no loop back-edge or guard, each wait covers exactly the loads
+    // its step needs (a back-edge or a join would wait for every load).
     constexpr int NB = 4;  // operand buffers: loads run NB - 1 steps ahead
     Step buf[NB];
 #pragma unroll
     for (int p = 1; p < NB; ++p) load_step(p, buf[p % NB]);
     __syncthreads();
 #pragma unroll
-    for (int p = 1; p < kMaxSegments; ++p) {
-        if (p >= P) continue;
+    for (int p = 1; p < P; ++p) {
         load_step(p + NB - 1, buf[(p + NB - 1) % NB]);
         const Step& cur = buf[p % NB];
         f32x4 b[KS];  // X_p[16 s + 4 q + e][m]
@@ -161,6 +160,7 @@ __global__ __launch_bounds__(DK * 4) void split_combine_kernel(const float* __re
         __syncthreads();
     }
     // X_p (p = 1 .. P-1) for the output correction, X_P = S_end(P-1) is the final state
+#pragma unroll
     for (int p = 1; p <= P; ++p) {
         float* dst = p < P ? xst + ((size_t)p * H + h) * sv : final_state;
         if (p == P) {
@@ -271,8 +271,19 @@ template <int DK, int DV>
 hipError_t launch_fix(const float* fin_a, const float* fin_b, float* xst, float* final_state,
                       const float* o_i, float* o, int64_t N, int H, int P, int64_t seg_chunks,
                       hipStream_t stream) {
-    hipLaunchKernelGGL((split_combine_kernel<DK>), dim3((unsigned)H, DV / 16), dim3(DK * 4), 0,
-                       stream, fin_a, fin_b, xst, final_state, P, H, DV);
+    const dim3 grid((unsigned)H, DV / 16), block(DK * 4);
+    switch (P) {
+#define KDA_COMBINE(NP)                                                                        \
+    case NP:                                                                                   \
+        hipLaunchKernelGGL((split_combine_kernel<DK, NP>), grid, block, 0, stream, fin_a, fin_b, \
+                           xst, final_state, H, DV);                                           \
+        break;
+        KDA_COMBINE(6) KDA_COMBINE(7) KDA_COMBINE(8) KDA_COMBINE(9) KDA_COMBINE(10)
+        KDA_COMBINE(11) KDA_COMBINE(12) KDA_COMBINE(13) KDA_COMBINE(14) KDA_COMBINE(15)
+        KDA_COMBINE(16)
+#undef KDA_COMBINE
+        default: return hipErrorInvalidValue;
+    }
     // chunks per workgroup: up to kMaxGroup, fewer when that leaves under
     // about four workgroups per CU
     const int64_t fix_chunks = (int64_t)(P - 1) * seg_chunks * H;
