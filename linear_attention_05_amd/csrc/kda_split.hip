@@ -179,11 +179,13 @@ __global__ __launch_bounds__(DK * 4) void split_combine_kernel(const float* __re
 // three passes of v_mfma_f32_16x16x32_f16 (hi hi, hi lo, lo hi) with fp32
 // accumulation: the dropped lo lo term is about 2^-22 of each product, so the
 // correction keeps fp32 accuracy at three times the fp16 rate instead of the
-// fp32 matrix-core rate (8x lower). One workgroup per (head, segment, group of
-// up to kMaxGroup chunks inside the segment); wave w owns value-column tiles
-// w + 4 j, whose X_p^T operand pairs stay in registers for the whole group.
+// fp32 matrix-core rate (8x lower). One workgroup per (head, segment, pair of
+// chunks inside the segment); wave w owns value-column tiles w + 4 j, whose
+// X_p^T operand pairs stay in registers. The eight 16-token tiles are fully
+// unrolled and each tile's oI rows and old o values are loaded one tile ahead
+// (straight-line code: the waits cover only the tile in use).
 // Fragments: lane l holds row (A) or column (B) l % 16 at K = 8 (l / 16) + e.
-constexpr int kMaxGroup = 8;
+constexpr int kGroup = 2;  // chunks per workgroup
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ _Float16 f16_hi(float x) { return (_Float16)x; }
@@ -193,19 +195,19 @@ template <int DK, int DV>
 __global__ __launch_bounds__(kT) void split_correct_kernel(const float* __restrict__ o_i,
                                                            const float* __restrict__ xst,
                                                            float* __restrict__ o, int64_t N, int H,
-                                                           int64_t seg_chunks, int64_t groups_per_seg,
-                                                           int group) {
+                                                           int64_t seg_chunks, int64_t groups_per_seg) {
     constexpr int CTW = DV / 64;  // column tiles per wave
     constexpr int KS = DK / 32;   // 32-wide K steps
+    constexpr int NTILE = kGroup * 4;
     const int h = (int)(blockIdx.x % (unsigned)H);
     const int64_t wg = (int64_t)(blockIdx.x / (unsigned)H);
     const int p = 1 + (int)(wg / groups_per_seg);
-    const int64_t nchunks = (N + 63) / 64;
-    const int64_t c0 = p * seg_chunks + (wg % groups_per_seg) * group;
-    int64_t c1 = c0 + group;
-    c1 = c1 < (p + 1) * seg_chunks ? c1 : (p + 1) * seg_chunks;
-    c1 = c1 < nchunks ? c1 : nchunks;
-    if (c0 >= c1) return;  // uniform over the workgroup
+    const int64_t c0 = p * seg_chunks + (wg % groups_per_seg) * kGroup;
+    // tokens of this workgroup that belong to segment p and exist
+    int64_t t_end = (p + 1) * seg_chunks * 64;
+    t_end = t_end < N ? t_end : N;
+    const int64_t t_begin = c0 * 64;
+    if (t_begin >= t_end) return;  // uniform over the workgroup
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int m = lane & 15, q = lane >> 4;
     // A = X_p^T: row 16 ct + m, K = 32 ks + 8 q + e
@@ -223,33 +225,46 @@ __global__ __launch_bounds__(kT) void split_correct_kernel(const float* __restri
                     alo[j][ks][e] = f16_lo(x);
                 }
     }
-    const int nt = (int)(c1 - c0) * 4;  // 16-token tiles
-    for (int u = 0; u < nt; ++u) {
-        const int64_t tok = c0 * 64 + 16 * u + m;
-        const bool ok = tok < N;
-        const int64_t row = (ok ? tok : 0) * H + h;
-        // B = oI^T: column = token 16 u + m, K = 32 ks + 8 q + e
-        half8 bhi[KS], blo[KS];
+    struct Tile {
+        f32x4 v[2 * KS];  // oI row pieces: K = 32 ks + 8 q + {0..3} and + {4..7}
+        f32x4 old[CTW];
+    };
+    // rows outside [t_begin, t_end) are read from t_begin (in bounds) and not stored
+    auto row_of = [&](int u) {
+        const int64_t tok = t_begin + 16 * u + m;
+        return (tok < t_end ? tok : t_begin) * H + h;
+    };
+    auto load_tile = [&](int u, Tile& tl) {
+        const int64_t row = row_of(u);
         const float* src = o_i + row * (int64_t)DK + 8 * q;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            const f32x4 v0 = *reinterpret_cast<const f32x4*>(src + 32 * ks);
-            const f32x4 v1 = *reinterpret_cast<const f32x4*>(src + 32 * ks + 4);
+            tl.v[2 * ks] = *reinterpret_cast<const f32x4*>(src + 32 * ks);
+            tl.v[2 * ks + 1] = *reinterpret_cast<const f32x4*>(src + 32 * ks + 4);
+        }
+        const float* dst = o + row * (int64_t)DV + 4 * q;
+#pragma unroll
+        for (int j = 0; j < CTW; ++j) tl.old[j] = *reinterpret_cast<const f32x4*>(dst + 16 * (wave + 4 * j));
+    };
+    Tile buf[2];
+    load_tile(0, buf[0]);
+#pragma unroll
+    for (int u = 0; u < NTILE; ++u) {
+        if (u + 1 < NTILE) load_tile(u + 1, buf[(u + 1) & 1]);
+        const Tile& cur = buf[u & 1];
+        half8 bhi[KS], blo[KS];  // B = oI^T: column = token, K = 32 ks + 8 q + e
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float x = ok ? (e < 4 ? v0[e] : v1[e - 4]) : 0.f;
+                const float x = e < 4 ? cur.v[2 * ks][e] : cur.v[2 * ks + 1][e - 4];
                 bhi[ks][e] = f16_hi(x);
                 blo[ks][e] = f16_lo(x);
             }
-        }
-        float* dst = o + row * (int64_t)DV + 4 * q;
-        f32x4 old[CTW];
-#pragma unroll
-        for (int j = 0; j < CTW; ++j) old[j] = *reinterpret_cast<const f32x4*>(dst + 16 * (wave + 4 * j));
         f32x4 acc[CTW][2];
 #pragma unroll
         for (int j = 0; j < CTW; ++j) {
-            acc[j][0] = old[j];
+            acc[j][0] = cur.old[j];
             acc[j][1] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
 #pragma unroll
@@ -260,10 +275,12 @@ __global__ __launch_bounds__(kT) void split_correct_kernel(const float* __restri
                 acc[j][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[j][ks], blo[ks], acc[j][1], 0, 0, 0);
                 acc[j][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[j][ks], bhi[ks], acc[j][1], 0, 0, 0);
             }
-        if (ok)
+        const int64_t tok = t_begin + 16 * u + m;
+        if (tok < t_end) {
+            float* dst = o + (tok * H + h) * (int64_t)DV + 4 * q;
 #pragma unroll
-            for (int j = 0; j < CTW; ++j)
-                *reinterpret_cast<f32x4*>(dst + 16 * (wave + 4 * j)) = acc[j][0] + acc[j][1];
+            for (int j = 0; j < CTW; ++j) *reinterpret_cast<f32x4*>(dst + 16 * (wave + 4 * j)) = acc[j][0] + acc[j][1];
+        }
     }
 }
 
@@ -284,16 +301,11 @@ hipError_t launch_fix(const float* fin_a, const float* fin_b, float* xst, float*
 #undef KDA_COMBINE
         default: return hipErrorInvalidValue;
     }
-    // chunks per workgroup: up to kMaxGroup, fewer when that leaves under
-    // about four workgroups per CU
-    const int64_t fix_chunks = (int64_t)(P - 1) * seg_chunks * H;
-    int64_t group = fix_chunks / (4 * kSizingCUs);
-    group = group < 1 ? 1 : (group > kMaxGroup ? kMaxGroup : group);
-    const int64_t groups_per_seg = (seg_chunks + group - 1) / group;
+    const int64_t groups_per_seg = (seg_chunks + kGroup - 1) / kGroup;
     const int64_t wgs = (int64_t)(P - 1) * groups_per_seg * H;
     if (wgs > 0)
         hipLaunchKernelGGL((split_correct_kernel<DK, DV>), dim3((unsigned)wgs), dim3(kT), 0, stream,
-                           o_i, xst, o, N, H, seg_chunks, groups_per_seg, (int)group);
+                           o_i, xst, o, N, H, seg_chunks, groups_per_seg);
     return hipGetLastError();
 }
 
