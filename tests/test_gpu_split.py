@@ -94,3 +94,22 @@ def test_segment_rule():
     assert K.kda_prefill_scan_segments(65536, 1, 8, 128, 128, bf) == 1
     assert K.kda_prefill_scan_segments(65536, 1, 1, 128, 128, bf) == 16
     assert K.kda_prefill_scan_segments(8192, 1, 1, 128, 128, bf, chunk_size=32) == 0
+
+
+def test_split_with_frontend():
+    """Raw inputs with the in-kernel front-end (K1 applies it; the scans and the
+    split path see the same handoff as for transformed inputs)."""
+    import torch
+    import linear_attention_05_amd as K
+    from oracle import frontend as fe
+    raw = make_prefill([4100], 2, 128, 128, "bf16", 781, raw=True)
+    plain = make_prefill([4100], 2, 128, 128, "bf16", 781, init_state=True)
+    assert segments(plain) >= 6
+    q, k, v, g, beta = (dev_tensor(a) for a in (raw.q, raw.k, raw.v, raw.g, raw.beta))
+    o, fs, _ = K.kda_prefill_chunked(q, k, v, g, beta, initial_state=dev_tensor(plain.initial_state),
+                                     frontend=fe.FRONT_ALL)
+    torch.cuda.synchronize()
+    r = recurrence.prefill(*fe.apply(raw.q, raw.k, raw.v, raw.g, raw.beta, fe.FRONT_ALL),
+                           raw.cu_seqlens, initial_state=plain.initial_state)
+    assert_parity(o.cpu().numpy(), r["o"], "bf16", "split o, front-end")
+    assert_parity(fs.cpu().numpy(), r["final"], "bf16", "split final state, front-end")
