@@ -316,7 +316,8 @@ __device__ __forceinline__ void locate_chunk(int ci, const int32_t* cu, const in
 // ---------------------------------------------------------------- K1 -----
 // One workgroup per (chunk, head). Phases, separated by barriers:
 //   stage   K and g into LDS (16-byte loads), beta; cumulative sum of g per
-//           channel in fp64, stored as G*log2(e) in place of g
+//           channel (fp32 for bf16 inputs, fp64 for fp32 inputs), stored as
+//           G*log2(e) in place of g
 //   A       the 10 lower 16x16 block pairs of A (to LDS) and of P (to the
 //           handoff); also the Qd, Kc^T and Gamma_last handoff
 //   inverse (I + A)^-1 by forward substitution, all four waves: wave w owns
@@ -361,7 +362,10 @@ __global__ __launch_bounds__(kThreads, BF16 ? 3 : 2) void k1_prep_kernel(
     __shared__ __attribute__((aligned(16))) unsigned char sKA[KBYTES > ABYTES ? KBYTES : ABYTES];
     __shared__ __attribute__((aligned(16))) float sG[C][GP];  // g, then G * log2(e)
     __shared__ float sB[C];
-    __shared__ double sTot[NQ][DK];
+    // cumulative-sum accumulator: fp32 for bf16 inputs (its rounding, about
+    // 64 ulp of G, is far below the fp16 operand rounding), fp64 for fp32 inputs
+    using GAcc = typename std::conditional<BF16, float, double>::type;
+    __shared__ GAcc sTot[NQ][DK];
     __shared__ float sQn[L2 ? C : 1];  // inverse query-row norms
     TIn(*sK)[KP] = reinterpret_cast<TIn(*)[KP]>(sKA);
     float(*sA)[AP] = reinterpret_cast<float(*)[AP]>(sKA);
@@ -396,8 +400,12 @@ __global__ __launch_bounds__(kThreads, BF16 ? 3 : 2) void k1_prep_kernel(
     const int rstride = H * DK;
     auto row_ptr = [&](const auto* p, int r) { return p + base0 + (r < len ? r : len - 1) * rstride; };
 
-    // ---- stage: K and g (zero past the chunk end), beta. Every load of the
-    // workgroup is issued before the first one is consumed.
+    // ---- stage: K, g (zero past the chunk end) and beta (zero past the end).
+    // Every load of the workgroup is issued before the first one is consumed.
+    // Key and query rows past the chunk end hold copies of its last row and
+    // need no zeroing: with beta = 0 on those rows, A, W and Ab vanish on
+    // them exactly (so do U's rows, which Kc's rows multiply), no output row
+    // past the end is stored, and P and A read them only at those rows.
     typedef TIn vecK_t __attribute__((ext_vector_type(VEC)));
     constexpr int KV = C * DK / VEC / kThreads;  // 16-byte K vectors per thread
     constexpr int GV = C * DK / 4 / kThreads;    // 16-byte g vectors per thread
@@ -408,7 +416,7 @@ __global__ __launch_bounds__(kThreads, BF16 ? 3 : 2) void k1_prep_kernel(
         const int i = t + u * kThreads;
         const int r = i / (DK / VEC), c = (i % (DK / VEC)) * VEC;
         const vecK_t kv = *reinterpret_cast<const vecK_t*>(row_ptr(K, r) + c);
-        kreg[u] = r < len ? kv : vecK_t{};
+        kreg[u] = kv;
     }
 #pragma unroll
     for (int u = 0; u < GV; ++u) {
@@ -435,7 +443,7 @@ __global__ __launch_bounds__(kThreads, BF16 ? 3 : 2) void k1_prep_kernel(
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
             const tin8 qv = *reinterpret_cast<const tin8*>(row_ptr(Q, r) + 32 * ks + 8 * q);
-            qa[gi][ks] = (rb >= 0 && r < len) ? qv : tin8{};
+            qa[gi][ks] = qv;
         }
     }
     constexpr int QDF = 4 * NKS / 4;  // Qd frags per wave
@@ -480,11 +488,11 @@ __global__ __launch_bounds__(kThreads, BF16 ? 3 : 2) void k1_prep_kernel(
     }
     __syncthreads();
     {
-        // inclusive cumulative sum per channel in fp64 (rows past the end add 0)
+        // inclusive cumulative sum per channel (rows past the end add 0)
         const int c = t % DK, grp = t / DK;
-        double acc = 0.0;
+        GAcc acc = 0;
 #pragma unroll
-        for (int r = grp * RPQ; r < (grp + 1) * RPQ; ++r) acc += (double)sG[r][c];
+        for (int r = grp * RPQ; r < (grp + 1) * RPQ; ++r) acc += (GAcc)sG[r][c];
         sTot[grp][c] = acc;
         if constexpr (L2) {  // key rows normalised in place: four threads per row
             constexpr int NV = DK / 4 / VEC;  // 16-byte vectors per thread
@@ -516,12 +524,12 @@ __global__ __launch_bounds__(kThreads, BF16 ? 3 : 2) void k1_prep_kernel(
             }
         }
         __syncthreads();
-        double run = 0.0;
+        GAcc run = 0;
         for (int p = 0; p < grp; ++p) run += sTot[p][c];
 #pragma unroll
         for (int r = grp * RPQ; r < (grp + 1) * RPQ; ++r) {
-            run += (double)sG[r][c];
-            sG[r][c] = (float)(run * 1.4426950408889634);
+            run += (GAcc)sG[r][c];
+            sG[r][c] = (float)(run * (GAcc)1.4426950408889634);
         }
     }
     __syncthreads();
@@ -548,7 +556,7 @@ __global__ __launch_bounds__(kThreads, BF16 ? 3 : 2) void k1_prep_kernel(
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
             const tin4 qv = *reinterpret_cast<const tin4*>(row_ptr(Q, r) + 32 * ks + 16 * hh + 4 * q);
-            qd[i][hh] = r < len ? qv : tin4{};
+            qd[i][hh] = qv;
         }
     }
 
