@@ -295,7 +295,8 @@ hipError_t launch_fix(const float* fin_a, const float* fin_b, float* xst, float*
         hipLaunchKernelGGL((split_combine_kernel<DK, NP>), grid, block, 0, stream, fin_a, fin_b, \
                            xst, final_state, H, DV);                                           \
         break;
-        KDA_COMBINE(6) KDA_COMBINE(7) KDA_COMBINE(8) KDA_COMBINE(9) KDA_COMBINE(10)
+        KDA_COMBINE(6) KDA_COMBINE(7) KDA_COMBINE(8) KDA_COMBINE(9)
+        KDA_COMBINE(10)
         KDA_COMBINE(11) KDA_COMBINE(12) KDA_COMBINE(13) KDA_COMBINE(14) KDA_COMBINE(15)
         KDA_COMBINE(16)
 #undef KDA_COMBINE
