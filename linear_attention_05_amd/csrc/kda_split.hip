@@ -321,7 +321,7 @@ int prefill_split_segments(int64_t total_tokens, int num_seqs, int H, int Dk, in
     P = P < kMaxSegments ? P : kMaxSegments;
     // two scans of 1/P of the chain plus the combine and the correction: measured
     // on MI355X (D = 128, T = 65536) 3.3x faster than the plain scan at P = 16,
-    // 1.7x at P = 8, 1.03x at P = 4 (before the combine and correction were tuned)
+    // 1.7x at P = 8, 1.05x at P = 4
     if (P < kMinSegments) return 1;
     const int64_t seg = (nchunks + P - 1) / P;
     return (int)((nchunks + seg - 1) / seg);
