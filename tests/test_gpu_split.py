@@ -113,3 +113,31 @@ def test_split_with_frontend():
                            raw.cu_seqlens, initial_state=plain.initial_state)
     assert_parity(o.cpu().numpy(), r["o"], "bf16", "split o, front-end")
     assert_parity(fs.cpu().numpy(), r["final"], "bf16", "split final state, front-end")
+
+
+@pytest.mark.parametrize("H,seed", [(4, 4242), (1, 4243)])
+def test_split_full_size_sampled(H, seed):
+    """The few-head workloads bench.py times (B=1, T=65536, D=128, bf16, S0),
+    through the chunk-parallel scan, on (head, 16-column) units the oracle
+    computes one by one over all 65536 tokens."""
+    T, D = 65536, 128
+    x = make_prefill([T], H, D, D, "bf16", seed, init_state=True)
+    P = segments(x)
+    print(f"split full-size H={H} T={T}: {P} segments", flush=True)
+    assert P >= 8
+    o, fs = run(x)
+    assert np.isfinite(o).all() and np.isfinite(fs).all()
+    units = sorted({(0, 0, 0), (0, H - 1, D // 16 - 1), (0, H // 2, 3)})
+    r = recurrence.prefill(x.q, x.k, x.v, x.g, x.beta, x.cu_seqlens,
+                           initial_state=x.initial_state,
+                           units=np.array(units, dtype=np.int32), col_block=16)
+    go, ro, gf, rf = [], [], [], []
+    for _, h, cb in units:
+        cols = slice(16 * cb, 16 * cb + 16)
+        go.append(o[:, h, cols].ravel())
+        ro.append(r["o"][:, h, cols].ravel())
+        gf.append(fs[0, h, :, cols].ravel())
+        rf.append(r["final"][0, h, :, cols].ravel())
+    res = (assert_parity(np.concatenate(go), np.concatenate(ro), "bf16", "o (sampled)"),
+           assert_parity(np.concatenate(gf), np.concatenate(rf), "bf16", "final (sampled)"))
+    print(res, flush=True)
