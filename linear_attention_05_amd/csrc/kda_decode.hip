@@ -291,7 +291,7 @@ __global__ __launch_bounds__(kThreads) void advance_kernel(
 
     // the (at most 63) rows the position still needs, staged once: their loads
     // are all in flight together instead of one token's worth per step
-    __shared__ __attribute__((aligned(16))) float s_g[63][DK], s_k[63][DK], s_v[63][DV];
+    __shared__ __attribute__((aligned(16))) float s_g[63][DK], s_k[63][DK], s_v[63][DV];  // s_g: alpha
     __shared__ float s_b[64];
 
     const int t = threadIdx.x;
@@ -354,10 +354,13 @@ __global__ __launch_bounds__(kThreads) void advance_kernel(
         const int idx = t + u * kThreads;
         const int i = idx / (DK / 4), c = 4 * (idx % (DK / 4));
         if (i < r) {
+            // decay factors alpha = e^g, formed here for all rows at once
+            // instead of on the token chain
             f32x4 gi = gv[u];
-            if (front & kFrontGate) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) gi[e] = -__expf(gi[e]);
+            for (int e = 0; e < 4; ++e) {
+                if (front & kFrontGate) gi[e] = -__expf(gi[e]);
+                gi[e] = __expf(gi[e]);
             }
             *reinterpret_cast<f32x4*>(&s_g[i][c]) = gi;
             *reinterpret_cast<f32x4*>(&s_k[i][c]) = kv[u];
@@ -411,7 +414,7 @@ __global__ __launch_bounds__(kThreads) void advance_kernel(
         f32x4 rr = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int m = 0; m < RPL; ++m) {
-            s[m] *= __expf(gc[m]);
+            s[m] *= gc[m];
             rr += s[m] * kc[m];
         }
 #pragma unroll
