@@ -1918,6 +1918,218 @@ __global__ __launch_bounds__(320) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
     }
 }
 
+// ---------------------------------------------------- position advance ----
+// States at arbitrary positions with bf16 inputs. The scan stored the state
+// S_n at the start of the chunk that holds position P; the first r = P mod 64
+// rows of that chunk advance it in chunk form on the matrix cores, from the
+// handoff K1 wrote for the chunk (rows < r of Ab and W involve only rows < r):
+//   U_r = rows < r of (Ab V - W S_n),
+//   S_P = Diag(e^{G_{r-1}}) S_n + Kc_r^T U_r,
+//   Kc_r[s][c] = k_s[c] e^{G_{r-1}[c] - G_s[c]} for s < r, 0 otherwise,
+// G the cumulative decay from the chunk start (the same chunk algebra as the
+// scan step, stopped after r rows). Kc_r is formed here from k and g: the
+// handoff's Kc is relative to the chunk end. One workgroup per (position,
+// head, 64 value columns), one 16-column tile per wave; operands as in the
+// scan (fp16, fp32 accumulation), S_n rounded to fp16 where it enters W S_n.
+template <int DK, int DV>
+__global__ __launch_bounds__(kThreads) void advance_chunk_kernel(
+    const void* __restrict__ kin, const void* __restrict__ vin, const float* __restrict__ g,
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ chunk_start, int num_seqs,
+    int64_t N, int H, int64_t max_chunks, const unsigned char* __restrict__ handoff, PosArgs pos,
+    unsigned front) {
+    using M = Mma<true>;
+    using E = _Float16;
+    using Frag = half8;
+    using HO = Handoff<DK, true>;
+    constexpr int NKS = DK / 32;  // 32-wide channel slabs
+    constexpr int NRT = DK / 16;  // 16-row channel tiles
+    constexpr int CT = DV / 16;   // value-column tiles
+    constexpr int KP = DK + 4;
+    constexpr int NQ = kThreads / DK;  // row groups of the cumulative sum
+    constexpr int RPQ = C / NQ;
+    constexpr int SP = DV + 4;
+    __shared__ __attribute__((aligned(16))) float sG[C][KP];  // G * log2(e); rows >= r: G_{r-1}
+    __shared__ __attribute__((aligned(16))) float sK[C][KP];  // keys (normalised with L2); rows >= r: 0
+    __shared__ __attribute__((aligned(16))) float sS[DK][SP];  // S_n
+    __shared__ float sTot[NQ][DK];
+
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int q = lane >> 4, m = lane & 15;
+    constexpr int NCH = (CT + 3) / 4;  // workgroups per (position, head): 64 columns each
+    const int half = (int)(blockIdx.x % (unsigned)NCH);
+    const int jh = (int)(blockIdx.x / (unsigned)NCH);
+    const int j = jh / H, h = jh % H;
+    int seq = 0;
+    int64_t st = 0, L = N;
+    if (cu) {  // sequence of position j: the last s with offsets[s] <= j
+        int lo = 0, hi = num_seqs - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (pos.offsets[mid] <= j) lo = mid;
+            else hi = mid - 1;
+        }
+        seq = lo;
+        seq_range(cu, seq, N, st, L);
+    }
+    int64_t P = pos.values[j];
+    P = P < 0 ? 0 : (P > L ? L : P);
+    const int r = (int)(P % C);
+    if (r == 0) return;  // the scan stored the exact state
+    const int64_t ci = (cu ? (int64_t)chunk_start[seq] : 0) + (P - r) / C;
+    const int64_t t0 = st + (P - r);
+    const E* hb = reinterpret_cast<const E*>(handoff + ((size_t)h * max_chunks + ci) * HO::kBytes);
+    float* S = pos.states + ((size_t)j * H + h) * (size_t)(DK * DV);
+
+    // this workgroup's 64 columns of S_n into LDS (16-byte loads, all issued
+    // before the decay and key work; the other column half belongs to another
+    // workgroup, which updates it in place)
+    constexpr int WC = DV < 64 ? DV : 64;  // columns per workgroup
+    constexpr int SV = DK * WC / 4 / kThreads;
+    f32x4 sreg[SV];
+#pragma unroll
+    for (int u = 0; u < SV; ++u) {
+        const int i = t + u * kThreads;
+        sreg[u] = *reinterpret_cast<const f32x4*>(S + (size_t)(i / (WC / 4)) * DV + WC * half + 4 * (i % (WC / 4)));
+    }
+#pragma unroll
+    for (int u = 0; u < SV; ++u) {
+        const int i = t + u * kThreads;
+        *reinterpret_cast<f32x4*>(&sS[i / (WC / 4)][WC * half + 4 * (i % (WC / 4))]) = sreg[u];
+    }
+
+    // ---- cumulative decay over rows < r (fp32, rows >= r add 0) and keys
+    {
+        const int c = t % DK, grp = t / DK;
+        float gl[RPQ];
+#pragma unroll
+        for (int i = 0; i < RPQ; ++i) {
+            const int row = grp * RPQ + i;
+            float x = row < r ? g[((t0 + row) * H + h) * DK + c] : 0.f;
+            if ((front & kFrontGate) && row < r) x = -__expf(x);
+            gl[i] = x;
+        }
+        float acc = 0.f;
+#pragma unroll
+        for (int i = 0; i < RPQ; ++i) acc += gl[i];
+        sTot[grp][c] = acc;
+        __syncthreads();
+        float run = 0.f;
+        for (int p = 0; p < grp; ++p) run += sTot[p][c];
+#pragma unroll
+        for (int i = 0; i < RPQ; ++i) {
+            run += gl[i];
+            sG[grp * RPQ + i][c] = run * kLog2e;
+        }
+    }
+    {  // keys: four threads per row, DK / 4 channels each, 16-byte loads
+        const int row = t >> 2, part = t & 3;
+        constexpr int NC = DK / 4;
+        const u16x8* src = reinterpret_cast<const u16x8*>(
+            static_cast<const unsigned short*>(kin) + ((t0 + (row < r ? row : 0)) * H + h) * DK + part * NC);
+        u16x8 raw[NC / 8];
+#pragma unroll
+        for (int v8 = 0; v8 < NC / 8; ++v8) raw[v8] = src[v8];
+        float kv[NC];
+        float ss = 0.f;
+#pragma unroll
+        for (int e = 0; e < NC; ++e) {
+            kv[e] = row < r ? bf16_to_f32(raw[e / 8][e % 8]) : 0.f;
+            ss += kv[e] * kv[e];
+        }
+        if (front & kFrontL2) {
+            ss += __shfl_xor(ss, 1);
+            ss += __shfl_xor(ss, 2);
+            const float inv = 1.f / sqrtf(ss + kL2Eps);
+#pragma unroll
+            for (int e = 0; e < NC; ++e) kv[e] *= inv;
+        }
+#pragma unroll
+        for (int e = 0; e < NC; ++e) sK[row][part * NC + e] = kv[e];
+    }
+    __syncthreads();
+
+    // Kc_r as A operands: rows = channels 16 ct + m, K = tokens of slab ts (permuted)
+    Frag kc[NRT][2];
+#pragma unroll
+    for (int ct = 0; ct < NRT; ++ct) {
+        const int c = 16 * ct + m;
+        const float gr = sG[r - 1][c];
+#pragma unroll
+        for (int ts = 0; ts < 2; ++ts)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int sr = 32 * ts + perm32(q, e);
+                kc[ct][ts][e] = (E)(sK[sr][c] * fast_exp2(gr - sG[sr][c]));
+            }
+    }
+
+    // Ab and -W operands: the same for every column tile, loaded once per wave
+    Frag abf[4][2], wnf[4][NKS];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+#pragma unroll
+        for (int ts = 0; ts < 2; ++ts) abf[rt][ts] = load_frag<Frag, E>(hb + HO::kAb, rt * 2 + ts, lane);
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) wnf[rt][ks] = load_frag<Frag, E>(hb + HO::kW, rt * NKS + ks, lane);
+    }
+
+    {
+        const int ctile = 4 * half + wave;
+        if (ctile >= CT) return;  // DV = 64 uses one workgroup of four tiles
+        const int col = 16 * ctile + m;
+        // B operands: S_n (K = channels) and V (K = tokens, rows clamped into the sequence data)
+        Frag sb[NKS], vb[2];
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sb[ks][e] = (E)sS[32 * ks + perm32(q, e)][col];
+#pragma unroll
+        for (int ts = 0; ts < 2; ++ts)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                int64_t row = t0 + 32 * ts + perm32(q, e);
+                row = row < N ? row : N - 1;
+                vb[ts][e] = (E)bf16_to_f32(static_cast<const unsigned short*>(vin)[(row * H + h) * DV + col]);
+            }
+        f32x4 old[NRT];  // S_n at this lane's result rows
+#pragma unroll
+        for (int ct = 0; ct < NRT; ++ct)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) old[ct][i] = sS[16 * ct + 4 * q + i][col];
+        // U = Ab V + (-W) S_n, row tiles of tokens
+        f32x4 u[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ts = 0; ts < 2; ++ts) acc = M::run(abf[rt][ts], vb[ts], acc);
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) acc = M::run(wnf[rt][ks], sb[ks], acc);
+            u[rt] = acc;
+        }
+        // two stacked U tiles are the B operand of one token slab
+        Frag ub[2];
+#pragma unroll
+        for (int ts = 0; ts < 2; ++ts)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                ub[ts][i] = (E)u[2 * ts][i];
+                ub[ts][4 + i] = (E)u[2 * ts + 1][i];
+            }
+#pragma unroll
+        for (int ct = 0; ct < NRT; ++ct) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ts = 0; ts < 2; ++ts) acc = M::run(kc[ct][ts], ub[ts], acc);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int c = 16 * ct + 4 * q + i;
+                S[(size_t)c * DV + col] = fast_exp2(sG[r - 1][c]) * old[ct][i] + acc[i];
+            }
+        }
+    }
+}
+
 // ------------------------------------------------------------- host side ---
 struct Plan {
     int32_t* chunk_start;
@@ -2051,7 +2263,11 @@ hipError_t launch_typed(const PrefillArgs& a, hipStream_t stream) {
         if (a.pos.num_pos > 0) {  // finish the states of positions inside a chunk
             const hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
-            return launch_advance(a, stream);
+            if (!BF16) return launch_advance(a, stream);  // fp32 inputs: token by token
+            hipLaunchKernelGGL((advance_chunk_kernel<DK, DV>), dim3((unsigned)((int64_t)a.pos.num_pos * a.H * (DV / 64))),
+                               dim3(kThreads), 0, stream, a.k, a.v, a.g, a.cu_seqlens,
+                               varlen ? p.chunk_start : nullptr, a.num_seqs, a.total_tokens, a.H,
+                               p.max_chunks, p.handoff, a.pos, a.frontend);
         }
     }
     return hipGetLastError();
