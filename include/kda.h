@@ -246,9 +246,12 @@ kda_status_t kda_prefill_chunked_ex(
  *                the first pos_values[j] tokens of its sequence
  *
  * The scan stores the state at the start of the chunk that holds each P and
- * a small kernel runs the remaining P mod 64 tokens of the recurrence on it
- * in fp32; both belong to the SCAN phase, which then also reads k, v, g and
- * beta, so a split call must pass the same `frontend` bits to both phases.
+ * a small kernel applies the remaining P mod 64 tokens to it: with bf16
+ * inputs in chunk form on the matrix cores, from that chunk's prepared
+ * tensors in the workspace and its k, v, g (the same fp16-operand numerics as
+ * the scan); with fp32 inputs token by token in fp32 (also reading beta).
+ * Both belong to the SCAN phase, so a split call must pass the same
+ * `frontend` bits to both phases.
  * Device-side (unchecked) preconditions: P outside [0, L_s] is clamped into
  * it; offsets outside [0, num_pos] are clamped; out-of-order positions give
  * unspecified states in their slots (never an out-of-bounds access).
