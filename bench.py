@@ -481,7 +481,8 @@ def main():
     # calls at the headline shape): the default warm-up covers that
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--decode-steps", type=int, default=64)
-    ap.add_argument("--only", choices=["all", "prefill", "decode", "few_heads"], default="all")
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "few_heads", "long_varlen"],
+                    default="all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra-workloads", action="store_true",
                     help="skip timing the long-context and varlen prefill workloads")
@@ -525,6 +526,11 @@ def main():
         del a, b
 
     out = {}
+    if args.only == "long_varlen":
+        out["prefill_workloads"] = [bench_prefill_workload(2), bench_prefill_workload(3)]
+        out["kernel_source_sha"] = kernel_source_sha()
+        print(json.dumps(out), flush=True)
+        return
     if args.only == "few_heads":
         out["few_heads"] = [bench_few_heads(4), bench_few_heads(1)]
         out["kernel_source_sha"] = kernel_source_sha()
