@@ -202,11 +202,20 @@ def cpu_baseline(x, target_s=10.0):
         spent += tn
         reps += 1
     full = float(np.median(per_head)) * x.H
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
+    # the recurrence's own work: 7 Dk Dv FLOPs per token-head (decay, retrieval,
+    # write, readout)
+    gflops = x.total_tokens * x.H * 7 * x.Dk * x.Dv / full / 1e9
     return dict(value=x.total_tokens / full / 1e6, unit="Mtok/s", cores=cores, kind="oracle",
                 sample=f"all {x.total_tokens} tokens x {n} of {x.H} heads x all {x.Dv} value "
                        f"columns, fp64 token recurrence, repeated {reps}x ({spent:.1f} s); "
                        f"median scaled to {x.H} heads",
-                seconds=spent)
+                seconds=spent, gflops=round(gflops, 2), cpu_model=cpu_model)
 
 
 def bench_few_heads(H=4, T=65536, D=128, reps=5):
