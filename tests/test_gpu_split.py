@@ -141,3 +141,44 @@ def test_split_full_size_sampled(H, seed):
     res = (assert_parity(np.concatenate(go), np.concatenate(ro), "bf16", "o (sampled)"),
            assert_parity(np.concatenate(gf), np.concatenate(rf), "bf16", "final (sampled)"))
     print(res, flush=True)
+
+
+def _split_config(seed):
+    rng = np.random.default_rng([910, seed])
+    H = int(rng.integers(1, 6))
+    Dk, Dv = (int(rng.choice([64, 128])), int(rng.choice([64, 128])))
+    T = int(rng.integers(2048, 9000))
+    dtype = str(rng.choice(["f32", "bf16"]))
+    init = bool(rng.random() < 0.7)
+    front = int(rng.integers(0, 8))
+    return H, Dk, Dv, T, dtype, init, front
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_split_random_configuration(seed):
+    """Seeded random one-sequence configurations (heads, head dimensions, length,
+    dtype, initial state, front-end bits); the ones the rule sends to the
+    chunk-parallel scan are compared with the oracle on every output."""
+    import torch
+    import linear_attention_05_amd as K
+    from oracle import frontend as fe
+    from synth.inputs import PrefillInputs
+    H, Dk, Dv, T, dtype, init, front = _split_config(seed)
+    plain = make_prefill([T], H, Dk, Dv, dtype, 3000 + seed, init_state=init)
+    raw = make_prefill([T], H, Dk, Dv, dtype, 3000 + seed, raw=True, init_state=init)
+    pick = lambda bit, name: getattr(raw if front & bit else plain, name)
+    x = PrefillInputs(dtype, H, Dk, Dv, [T], pick(fe.FRONT_L2NORM_QK, "q"),
+                      pick(fe.FRONT_L2NORM_QK, "k"), plain.v, pick(fe.FRONT_GATE, "g"),
+                      pick(fe.FRONT_BETA_SIGMOID, "beta"), plain.initial_state)
+    P = segments(x)
+    print(f"split random seed {seed}: H={H} Dk={Dk} Dv={Dv} T={T} {dtype} init={init} "
+          f"front={front}: {P} segments", flush=True)
+    s0 = dev_tensor(x.initial_state) if init else None
+    o, fs, _ = K.kda_prefill_chunked(dev_tensor(x.q), dev_tensor(x.k), dev_tensor(x.v),
+                                     dev_tensor(x.g), dev_tensor(x.beta), initial_state=s0,
+                                     frontend=front)
+    torch.cuda.synchronize()
+    r = recurrence.prefill(*fe.apply(x.q, x.k, x.v, x.g, x.beta, front), x.cu_seqlens,
+                           initial_state=x.initial_state if init else None)
+    assert_parity(o.cpu().numpy(), r["o"], dtype, "o")
+    assert_parity(fs.cpu().numpy(), r["final"], dtype, "final state")
