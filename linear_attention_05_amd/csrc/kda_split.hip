@@ -17,10 +17,11 @@
 //   3. combine (fp32, sequential over segments): scan A already started
 //      segment 0 from S_0, so S_end(0) = F_0; for p >= 1 the true start state
 //      is X_p = S_end(p-1) and S_end(p) = M_p X_p + F_p;
-//   4. correct: o_t += oI_t X_p for every token of segments 1 .. P-1 (fp32).
+//   4. correct: o_t += oI_t X_p for every token of segments 1 .. P-1.
 // Both scans run P * H * D / 16 column blocks at once over chains P times
-// shorter. Everything here is fp32 except the scans themselves, which are the
-// plain path's kernels.
+// shorter; they are the plain path's kernels. The combine runs on fp32
+// matrix cores and the correction at fp32 accuracy (three fp16 passes on
+// hi/lo operand pairs, fp32 accumulation).
 #include "kda_internal.h"
 
 namespace kda {
