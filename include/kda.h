@@ -43,9 +43,17 @@
  *     violation gives unspecified results, never an out-of-bounds access,
  *     because sequence ranges are clamped to [0, total_tokens) on the device):
  *     cu_seqlens non-decreasing with cu_seqlens[num_seqs] == total_tokens;
- *     finite inputs; g <= 0; within a chunk of 64 tokens the decay summed over
- *     any 16 consecutive tokens stays below about 11 nats per channel when
- *     q/k/v are bf16 (fp16 operand range) and below about 80 nats for fp32.
+ *     g <= 0, where any such value is valid, -inf (alpha = 0) included; every
+ *     other input finite. With bf16 q/k/v the matrix-core operands are fp16,
+ *     so every element of v, of the states (the initial state and the state
+ *     at each 64-token chunk boundary) and of the pseudo-values
+ *     U = Ainv diag(beta) (V - K_decayed S) must have magnitude below 65504.
+ *   - Decay range: the prefill keeps every decay factor it forms at or below
+ *     1, so KDA's per-channel forgetting is handled down to alpha = 0 in any
+ *     channel. It floors the per-token log-decay at -16 nats with bf16 q/k/v
+ *     and at -64 nats with fp32 q/k/v (alpha >= 1.1e-7 resp. 1.6e-28); the
+ *     results change by less than 1.2e-7 of the largest state entry. The
+ *     decode step applies exp(g) as given.
  *   - The library keeps no global state besides the loaded code object and
  *     is reentrant; calls on different streams may run concurrently if they
  *     write disjoint outputs and workspaces.
@@ -215,8 +223,8 @@ kda_status_t kda_prefill_chunked_phases(
  * kda_prefill_chunked_phases with a `frontend` mask (a subset of the
  * KDA_FRONT_* bits; 0 = kda_prefill_chunked_phases). The transforms act in
  * the PREPARE phase, the only one that reads q, k, g and beta here; a
- * SCAN-only call ignores them. The documented decay precondition then
- * applies to -exp(u). Returns KDA_ERR_INVALID_ARG for unknown bits,
+ * SCAN-only call ignores them. The decay floor then applies to -exp(u)
+ * (u = +inf gives alpha = 0). Returns KDA_ERR_INVALID_ARG for unknown bits,
  * otherwise as kda_prefill_chunked_phases.
  */
 kda_status_t kda_prefill_chunked_ex(

@@ -5,6 +5,39 @@
 
 #include "kda_internal.h"
 
+#include <atomic>
+#include <mutex>
+
+namespace kda {
+
+DeviceInfo device_info() {
+    constexpr int kMaxDevices = 64;
+    static std::atomic<bool> ready[kMaxDevices];
+    static DeviceInfo info[kMaxDevices];
+    static std::mutex mu;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return DeviceInfo{};
+    if (ready[dev].load(std::memory_order_acquire)) return info[dev];
+    std::lock_guard<std::mutex> lock(mu);
+    if (!ready[dev].load(std::memory_order_relaxed)) {
+        DeviceInfo d;
+        int n = 0;
+        bool ok = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0;
+        if (ok) d.cus = n;
+        ok = ok && hipDeviceGetAttribute(&n, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) == hipSuccess && n > 0;
+        if (ok) d.lds_per_block = n;
+        ok = ok && hipDeviceGetAttribute(&n, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) == hipSuccess && n > 0;
+        if (ok) d.lds_per_cu = n;
+        d.valid = ok;
+        if (!ok) return d;  // not cached: asked again next time
+        info[dev] = d;
+        ready[dev].store(true, std::memory_order_release);
+    }
+    return info[dev];
+}
+
+}  // namespace kda
+
 namespace {
 
 constexpr int kVersion = 300;  // 0.3.0
@@ -66,10 +99,9 @@ int32_t kda_prefill_scan_segments(int64_t total_tokens, int32_t num_seqs, int32_
                                   int32_t Dv, int32_t chunk_size, kda_dtype_t in_dtype) {
     if (check_prefill_sizes(total_tokens, num_seqs, H, Dk, Dv, chunk_size, in_dtype) != KDA_OK)
         return 0;
-    int cus = 0, dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-        return 1;
+    const kda::DeviceInfo di = kda::device_info();
+    if (!di.valid) return 1;
+    const int cus = di.cus;
     const int want = kda::prefill_split_segments(total_tokens, num_seqs, H, Dk, Dv, cus);
     const int sized = kda::prefill_split_segments(total_tokens, num_seqs, H, Dk, Dv, kda::kSizingCUs);
     const int P = want < sized ? want : sized;

@@ -226,13 +226,9 @@ unsigned residency_pad() {
     constexpr int CG = DV / 4;
     constexpr int kStatic = 3 * kThreads * 4 + kWaves * CG * 2 * 16 + kWaves * 4;
     const int n = (DK * DV * 4 >= 65536) ? 1 : 65536 / (DK * DV * 4);
-    int lds = 0, dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return 0;
-    if (hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) != hipSuccess || lds <= 0)
-        return 0;
-    int per_block = 0;
-    if (hipDeviceGetAttribute(&per_block, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
-        return 0;
+    const DeviceInfo di = device_info();
+    if (!di.valid || di.lds_per_cu <= 0) return 0;
+    const int lds = di.lds_per_cu, per_block = di.lds_per_block;
     const int64_t want = (int64_t)lds * 2 / (2 * n + 1) - kStatic;
     if (want <= 0 || want + kStatic > per_block) return 0;  // cannot pad: default residency
     return (unsigned)want;

@@ -15,6 +15,18 @@ constexpr unsigned kFrontL2 = 1u, kFrontGate = 2u, kFrontBeta = 4u;
 constexpr unsigned kFrontAll = kFrontL2 | kFrontGate | kFrontBeta;
 constexpr float kL2Eps = 1e-6f;
 
+// Attributes of the current device the launches depend on, queried once per
+// device and process (later calls read the cached copy; hipGetDevice only).
+// `valid` is false when the runtime could not be queried; the other fields
+// then hold MI355X values.
+struct DeviceInfo {
+    bool valid = false;
+    int cus = 256;                // compute units
+    int lds_per_block = 65536;    // bytes of LDS one workgroup may use
+    int lds_per_cu = 0;           // bytes of LDS per CU (0: unknown)
+};
+DeviceInfo device_info();
+
 // ---- decode ---------------------------------------------------------------
 hipError_t launch_decode(const void* q, const void* k, const void* v, bool bf16,
                          const float* g, const float* beta, int B, int H, int Dk, int Dv,

@@ -22,9 +22,27 @@
 // (one pass of v_mfma_f32_16x16x32_f16; fp16 keeps 11 significant bits, 8x
 // finer than bf16, at the same matrix-core rate), S and U entering their
 // products rounded to fp16 once. With fp32 q/k/v every product runs on
-// v_mfma_f32_16x16x4_f32 with fp32 operands. Decay factors are formed as
-// e^(G_r - G_ref) with a reference row per 16-row block, so the products
-// never form e^(+G) of a whole chunk.
+// v_mfma_f32_16x16x4_f32 with fp32 operands.
+//
+// Decay range. Every decay factor an operand carries is e^(G_a - G_b) with
+// a >= b, i.e. at most 1, so no operand overflows for any g <= 0 and a factor
+// that underflows is off by less than the operand type's smallest step. A
+// pair (r, s) of rows in different 16-row blocks splits at the first row of
+// r's block (both halves <= 1). Inside a diagonal 16-row block the split
+// row must lie between s and r, which no single reference does for all
+// pairs; when the decay summed over the block is small in every channel
+// (below 2^12 for fp16 operands) the block still uses its first row (factors
+// in [2^-12, 2^12]: fp16 keeps full precision), otherwise the block is done
+// as four products, one per bit of the 16-row index: at level h the rows
+// with bit h set take e^(G_r - G_{start of r's h-run}) and the rows with bit
+// h clear take e^(G_{start of the next h-run} - G_s), and each product keeps
+// only the pairs whose highest differing index bit is h. The per-token
+// log-decay is floored at -kGFloor nats (alpha >= e^-16 for bf16 inputs,
+// e^-64 for fp32: the change it makes to any result is below 1e-7 of the
+// state), which keeps |G| over a chunk small enough that differences of the
+// stored G (fp32 for bf16 inputs, fp64 for fp32 inputs, from an fp64
+// cumulative sum) lose at most 1.2e-4 of a factor's log2, below the fp16
+// operand rounding.
 //
 // Fragment convention (both operand types). A 16 x 32 (M x K) A-operand tile
 // and a 32 x 16 (K x N) B-operand tile are held as 8 values per lane: lane l
@@ -54,6 +72,11 @@ typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
 constexpr int C = kChunk;      // 64 tokens per chunk
 constexpr int kThreads = 256;  // 4 waves
 constexpr float kLog2e = 1.4426950408889634f;
+// per-token log-decay floor (nats), by input type (see "Decay range" above)
+constexpr float kGFloorBF16 = 16.f, kGFloorF32 = 64.f;
+// a diagonal 16-row block keeps one reference row while the decay summed
+// over it stays below this many powers of two in every channel
+constexpr float kSpanLog2BF16 = 12.f, kSpanLog2F32 = 60.f;
 
 
 __device__ __forceinline__ float bf16_to_f32(unsigned short b) {
@@ -171,67 +194,167 @@ __device__ __forceinline__ void seq_range(const int32_t* cu, int s, int64_t N, i
 }
 
 // ------------------------------------------------------------ varlen prep ----
-// One workgroup: chunk_start = exclusive scan of ceil(L/64), ckpt_base =
-// exclusive scan of floor(L/interval), order = sequences by decreasing length
-// (ties by index) so that K2 starts the longest scans first.
-__global__ __launch_bounds__(kThreads) void prep_kernel(const int32_t* __restrict__ cu, int num_seqs,
-                                                        int64_t N, int64_t interval,
-                                                        int32_t* __restrict__ chunk_start,
-                                                        int32_t* __restrict__ ckpt_base,
-                                                        int32_t* __restrict__ order) {
-    __shared__ int32_t sc[kThreads], sk[kThreads];
-    __shared__ int32_t carry_c, carry_k;
-    const int t = threadIdx.x;
-    if (t == 0) {
-        carry_c = 0;
-        carry_k = 0;
-    }
+// One workgroup of 1024 threads; two passes over the sequences in tiles of
+// 8192 (8 consecutive sequences per thread), O(num_seqs) work:
+//   pass 1  chunk_start = exclusive scan of ceil(L/64) and ckpt_base =
+//           exclusive scan of floor(L/interval) (thread sums, wave scans, then
+//           the 16 wave totals), and a histogram of the sequences' length
+//           classes (half octaves of the chunk count)
+//   pass 2  order = sequences by decreasing length class, ties by index, so
+//           that K2 starts the longest scans first: a stable counting sort,
+//           ranks among equal classes within a wave from lane ballots and
+//           across waves and tiles from per-class counters.
+constexpr int kPrepThreads = 1024;
+constexpr int kPrepWaves = kPrepThreads / 64;
+constexpr int kPrepPer = 8;                              // sequences per thread and tile
+constexpr int kPrepTile = kPrepThreads * kPrepPer;
+constexpr int kClasses = 64;
+
+// Length class of a sequence of nc chunks: nc itself below 4, then two
+// classes per octave (nc < 2^26 gives at most 51). Non-decreasing in nc.
+__device__ __forceinline__ int length_class(int nc) {
+    if (nc < 4) return nc;
+    const int e = 31 - __clz(nc);
+    return 2 * e + ((nc >> (e - 1)) & 1);
+}
+
+__global__ __launch_bounds__(kPrepThreads) void prep_kernel(const int32_t* __restrict__ cu, int num_seqs,
+                                                            int64_t N, int64_t interval,
+                                                            int32_t* __restrict__ chunk_start,
+                                                            int32_t* __restrict__ ckpt_base,
+                                                            int32_t* __restrict__ order) {
+    __shared__ int sWsum[2][kPrepWaves];          // per-wave totals of a tile
+    __shared__ int sHist[kClasses];               // sequences per class
+    __shared__ int sBase[kClasses];               // next order slot of each class
+    __shared__ int sWcnt[kPrepWaves][kClasses];   // pass 2: per-wave class counts
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    auto chunks_of = [&](int s, int64_t& L) {
+        int64_t st;
+        seq_range(cu, s, N, st, L);
+        return (int)((L + C - 1) / C);
+    };
+    for (int i = t; i < kClasses; i += kPrepThreads) sHist[i] = 0;
+    for (int i = t; i < kPrepWaves * kClasses; i += kPrepThreads) sWcnt[i / kClasses][i % kClasses] = 0;
     __syncthreads();
-    for (int base = 0; base < num_seqs; base += kThreads) {
-        const int s = base + t;
-        int nc = 0, nk = 0;
-        if (s < num_seqs) {
-            int64_t st, L;
-            seq_range(cu, s, N, st, L);
-            nc = (int)((L + C - 1) / C);
-            nk = interval > 0 ? (int)(L / interval) : 0;
+
+    // ---- pass 1: chunk and checkpoint offsets, class histogram
+    int carry_c = 0, carry_k = 0;  // the same in every thread
+    for (int base = 0; base < num_seqs; base += kPrepTile) {
+        const int s0 = base + t * kPrepPer;
+        int nc[kPrepPer], nk[kPrepPer], sc = 0, sk = 0;
+#pragma unroll
+        for (int e = 0; e < kPrepPer; ++e) {
+            nc[e] = 0;
+            nk[e] = 0;
+            if (s0 + e < num_seqs) {
+                int64_t L;
+                nc[e] = chunks_of(s0 + e, L);
+                nk[e] = interval > 0 ? (int)(L / interval) : 0;
+                atomicAdd(&sHist[length_class(nc[e])], 1);
+            }
+            sc += nc[e];
+            sk += nk[e];
         }
-        sc[t] = nc;
-        sk[t] = nk;
+        int ic = sc, ik = sk;  // inclusive scans over the wave
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int a = __shfl_up(ic, off), b = __shfl_up(ik, off);
+            if (lane >= off) {
+                ic += a;
+                ik += b;
+            }
+        }
+        if (lane == 63) {
+            sWsum[0][wave] = ic;
+            sWsum[1][wave] = ik;
+        }
         __syncthreads();
-        for (int off = 1; off < kThreads; off <<= 1) {  // inclusive Hillis-Steele scan
-            const int a = t >= off ? sc[t - off] : 0;
-            const int b = t >= off ? sk[t - off] : 0;
-            __syncthreads();
-            sc[t] += a;
-            sk[t] += b;
-            __syncthreads();
+        int wc = 0, wk = 0, tc = 0, tk = 0;
+#pragma unroll
+        for (int w = 0; w < kPrepWaves; ++w) {
+            const int a = sWsum[0][w], b = sWsum[1][w];
+            wc += w < wave ? a : 0;
+            wk += w < wave ? b : 0;
+            tc += a;
+            tk += b;
         }
-        if (s < num_seqs) {
-            chunk_start[s] = carry_c + sc[t] - nc;
-            ckpt_base[s] = carry_k + sk[t] - nk;
+        int pc = carry_c + wc + ic - sc, pk = carry_k + wk + ik - sk;
+#pragma unroll
+        for (int e = 0; e < kPrepPer; ++e) {
+            if (s0 + e < num_seqs) {
+                chunk_start[s0 + e] = pc;
+                ckpt_base[s0 + e] = pk;
+            }
+            pc += nc[e];
+            pk += nk[e];
         }
-        __syncthreads();
-        if (t == kThreads - 1) {
-            carry_c += sc[t];
-            carry_k += sk[t];
-        }
-        __syncthreads();
+        carry_c += tc;
+        carry_k += tk;
+        __syncthreads();  // sWsum is rewritten by the next tile
     }
     if (t == 0) {
         chunk_start[num_seqs] = carry_c;
         ckpt_base[num_seqs] = carry_k;
     }
-    for (int s = t; s < num_seqs; s += kThreads) {
-        int64_t st, L;
-        seq_range(cu, s, N, st, L);
-        int rank = 0;
-        for (int r = 0; r < num_seqs; ++r) {
-            int64_t str, Lr;
-            seq_range(cu, r, N, str, Lr);
-            rank += (Lr > L) || (Lr == L && r < s);
+    if (wave == 0) {  // first slot of each class: classes in decreasing order
+        const int cls = kClasses - 1 - lane;
+        const int v = sHist[cls];
+        int inc = v;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int a = __shfl_up(inc, off);
+            if (lane >= off) inc += a;
         }
-        order[rank] = s;
+        sBase[cls] = inc - v;
+    }
+    __syncthreads();
+
+    // ---- pass 2: order. Wave w takes sequences base + 512 w .. +511 of a
+    // tile, 64 at a time in index order.
+    constexpr int kPerWave = kPrepTile / kPrepWaves;
+    for (int base = 0; base < num_seqs; base += kPrepTile) {
+        int cls[kPrepPer], rank[kPrepPer];
+#pragma unroll
+        for (int i = 0; i < kPrepPer; ++i) {
+            const int s = base + wave * kPerWave + 64 * i + lane;
+            int c = -1;
+            if (s < num_seqs) {
+                int64_t L;
+                c = length_class(chunks_of(s, L));
+            }
+            cls[i] = c;
+            int r = 0;
+            // one round per distinct class among the 64 lanes: rank = earlier
+            // lanes of that class + the wave's count of it so far
+            for (unsigned long long todo = __ballot(c >= 0); todo;) {
+                const int leader = __builtin_ctzll(todo);
+                const int lc = __shfl(c, leader);
+                const unsigned long long same = __ballot(c == lc);
+                const int before = sWcnt[wave][lc];
+                if (c == lc) r = before + __popcll(same & ((1ull << lane) - 1ull));
+                if (lane == leader) sWcnt[wave][lc] = before + __popcll(same);
+                todo &= ~same;
+            }
+            rank[i] = r;
+        }
+        __syncthreads();
+        if (t < kClasses) {  // per class: exclusive prefix over the waves, from the running slot
+            int run = sBase[t];
+#pragma unroll
+            for (int w = 0; w < kPrepWaves; ++w) {
+                const int n = sWcnt[w][t];
+                sWcnt[w][t] = run;
+                run += n;
+            }
+            sBase[t] = run;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < kPrepPer; ++i)
+            if (cls[i] >= 0) order[sWcnt[wave][cls[i]] + rank[i]] = base + wave * kPerWave + 64 * i + lane;
+        __syncthreads();
+        for (int i = t; i < kPrepWaves * kClasses; i += kPrepThreads) sWcnt[i / kClasses][i % kClasses] = 0;
+        __syncthreads();
     }
 }
 
@@ -315,9 +438,11 @@ __device__ __forceinline__ void locate_chunk(int ci, const int32_t* cu, const in
 
 // ---------------------------------------------------------------- K1 -----
 // One workgroup per (chunk, head). Phases, separated by barriers:
-//   stage   K and g into LDS (16-byte loads), beta; cumulative sum of g per
-//           channel (fp32 for bf16 inputs, fp64 for fp32 inputs), stored as
-//           G*log2(e) in place of g
+//   stage   K and g into LDS (16-byte loads), beta; g floored at -kGFloor;
+//           cumulative sum of g per channel in fp64, stored as G*log2(e) in
+//           place of g (fp32 for bf16 inputs, fp64 for fp32 inputs); which
+//           diagonal 16-row blocks decay by more than 2^kSpanLog2 in some
+//           channel (those take the four-level products)
 //   A       the 10 lower 16x16 block pairs of A (to LDS) and of P (to the
 //           handoff); also the Qd, Kc^T and Gamma_last handoff
 //   inverse (I + A)^-1 by forward substitution, all four waves: wave w owns
@@ -335,7 +460,7 @@ __device__ __forceinline__ void locate_chunk(int ci, const int32_t* cu, const in
 // reads g as u and uses -exp(u), bit kFrontBeta reads beta as a logit and
 // uses its sigmoid.
 template <int DK, bool BF16, bool L2>
-__global__ __launch_bounds__(kThreads, BF16 ? 3 : 2) void k1_prep_kernel(
+__global__ __launch_bounds__(kThreads, BF16 ? 3 : (DK == 128 ? 1 : 2)) void k1_prep_kernel(
     const void* __restrict__ qin, const void* __restrict__ kin, const float* __restrict__ g,
     const float* __restrict__ beta, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ chunk_start, int num_seqs, int64_t N, int H, int64_t max_chunks,
@@ -360,12 +485,13 @@ __global__ __launch_bounds__(kThreads, BF16 ? 3 : 2) void k1_prep_kernel(
     constexpr int KBYTES = C * KP * (int)sizeof(TIn);
     constexpr int ABYTES = C * AP * (int)sizeof(float);
     __shared__ __attribute__((aligned(16))) unsigned char sKA[KBYTES > ABYTES ? KBYTES : ABYTES];
-    __shared__ __attribute__((aligned(16))) float sG[C][GP];  // g, then G * log2(e)
+    // G * log2(e): fp32 for bf16 inputs, fp64 for fp32 inputs (whose 1e-5
+    // results need differences of G exact to about 1e-9)
+    using GS = typename std::conditional<BF16, float, double>::type;
+    __shared__ __attribute__((aligned(16))) GS sG[C][GP];  // g, then G * log2(e)
     __shared__ float sB[C];
-    // cumulative-sum accumulator: fp32 for bf16 inputs (its rounding, about
-    // 64 ulp of G, is far below the fp16 operand rounding), fp64 for fp32 inputs
-    using GAcc = typename std::conditional<BF16, float, double>::type;
-    __shared__ GAcc sTot[NQ][DK];
+    __shared__ double sTot[NQ][DK];  // cumulative-sum partial totals
+    __shared__ unsigned sSlow;       // bit b: diagonal block b needs the four-level products
     __shared__ float sQn[L2 ? C : 1];  // inverse query-row norms
     TIn(*sK)[KP] = reinterpret_cast<TIn(*)[KP]>(sKA);
     float(*sA)[AP] = reinterpret_cast<float(*)[AP]>(sKA);
@@ -463,8 +589,16 @@ __global__ __launch_bounds__(kThreads, BF16 ? 3 : 2) void k1_prep_kernel(
 #pragma unroll
             for (int e = 0; e < 4; ++e) gv[e] = -__expf(gv[e]);
         }
-        *reinterpret_cast<f32x4*>(&sG[r][c]) = gv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) gv[e] = fmaxf(gv[e], BF16 ? -kGFloorBF16 : -kGFloorF32);
+        if constexpr (BF16) {
+            *reinterpret_cast<f32x4*>(&sG[r][c]) = gv;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sG[r][c + e] = (double)gv[e];
+        }
     }
+    if (t == 0) sSlow = 0u;
     if (t < C) sB[t] = ((front & kFrontBeta) && t < len) ? 1.f / (1.f + __expf(-breg)) : breg;
     // inverse query-row norms from this wave's phase-A rows: the four lanes
     // m + 16q hold the channels of row 16 rb + m between them
@@ -490,9 +624,9 @@ __global__ __launch_bounds__(kThreads, BF16 ? 3 : 2) void k1_prep_kernel(
     {
         // inclusive cumulative sum per channel (rows past the end add 0)
         const int c = t % DK, grp = t / DK;
-        GAcc acc = 0;
+        double acc = 0;
 #pragma unroll
-        for (int r = grp * RPQ; r < (grp + 1) * RPQ; ++r) acc += (GAcc)sG[r][c];
+        for (int r = grp * RPQ; r < (grp + 1) * RPQ; ++r) acc += (double)sG[r][c];
         sTot[grp][c] = acc;
         if constexpr (L2) {  // key rows normalised in place: four threads per row
             constexpr int NV = DK / 4 / VEC;  // 16-byte vectors per thread
@@ -524,12 +658,20 @@ __global__ __launch_bounds__(kThreads, BF16 ? 3 : 2) void k1_prep_kernel(
             }
         }
         __syncthreads();
-        GAcc run = 0;
+        double run = 0;
         for (int p = 0; p < grp; ++p) run += sTot[p][c];
+        static_assert(RPQ % 16 == 0, "a row group holds whole 16-row blocks");
+        GS first = 0;
 #pragma unroll
-        for (int r = grp * RPQ; r < (grp + 1) * RPQ; ++r) {
-            run += (GAcc)sG[r][c];
-            sG[r][c] = (float)(run * (GAcc)1.4426950408889634);
+        for (int i = 0; i < RPQ; ++i) {
+            const int r = grp * RPQ + i;
+            run += (double)sG[r][c];
+            const GS val = (GS)(run * 1.4426950408889634);
+            sG[r][c] = val;
+            // decay over the 16-row block in this channel (G is non-increasing)
+            if (i % 16 == 0) first = val;
+            if (i % 16 == 15 && first - val > (GS)(BF16 ? kSpanLog2BF16 : kSpanLog2F32))
+                atomicOr(&sSlow, 1u << (grp * (RPQ / 16) + i / 16));
         }
     }
     __syncthreads();
@@ -542,6 +684,8 @@ __global__ __launch_bounds__(kThreads, BF16 ? 3 : 2) void k1_prep_kernel(
         if constexpr (BF16) return bf16_to_f32(v);
         else return v;
     };
+    // (G_a - G_b) * log2(e) in channel c, differenced in the stored precision
+    auto gdiff = [&](int a, int b, int c) -> float { return (float)(sG[a][c] - sG[b][c]); };
 
     f32x4 aT[4];  // A tiles of this wave's block pairs (slot 2*gi + k2)
 
@@ -563,8 +707,44 @@ __global__ __launch_bounds__(kThreads, BF16 ? 3 : 2) void k1_prep_kernel(
     // ---- phase A: 16x16 block pairs (rb, sb), sb <= rb, reference row 16*rb:
     // every factor e^(G_r - G_ref) (r >= ref) is <= 1 and e^(G_ref - G_s) is
     // <= 1 for s < ref. Waves take the pairs grouped by rb so the row-block
-    // operands X = Kd', Z = Qd' are built once per rb.
+    // operands X = Kd', Z = Qd' are built once per rb. A diagonal pair whose
+    // block decays too much in some channel takes the four-level products.
+    const unsigned slow_blocks = __builtin_amdgcn_readfirstlane(sSlow);
     {
+        // A[r'][s'] with r' = 16rb + 4q + i, s' = 16sb + m, kept in registers
+        // until every wave is done reading K; P^T[s'][r'] with s' = 16sb + 4q + i,
+        // r' = 16rb + m -> P A-frag [rt = rb][slab sb/2], slots 4*(sb%2) + i of
+        // lane (m + 16q).
+        auto store_pair = [&](int gi, int k2, int rb, int sb, const f32x4& accA, const f32x4& accP) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int rr = 16 * rb + 4 * q + i, ss = 16 * sb + m;
+                aT[2 * gi + k2][i] = ss < rr ? sB[rr] * accA[i] : 0.f;
+            }
+            typedef E e4 __attribute__((ext_vector_type(4)));
+            e4 pv;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int ss = 16 * sb + 4 * q + i, rr = 16 * rb + m;
+                pv[i] = (E)(ss <= rr ? accP[i] : 0.f);
+            }
+            *reinterpret_cast<e4*>(hb + HO::kP + ((size_t)(rb * 2 + sb / 2) * 64 + lane) * 8 + 4 * (sb % 2)) = pv;
+        };
+        // Qd A-frags (first, so that the prefetched queries die early): rows tokens (tile rt), K channels (slab ks, permuted)
+#pragma unroll
+        for (int i = 0; i < QDF; ++i) {
+            const int f = wave + 4 * i;
+            const int rt = f / NKS, ks = f % NKS;
+            const int r = 16 * rt + m;
+            // perm32(q, e): channels 32ks + 4q + e (e < 4) and 32ks + 16 + 4q + e - 4
+            Frag out;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int c = 32 * ks + perm32(q, e);
+                out[e] = (E)(qf(qd[i][e >> 2][e & 3]) * (L2 ? sQn[r] : 1.f) * fast_exp2((float)sG[r][c]));
+            }
+            store_frag<Frag, E>(hb + HO::kQd, rt * NKS + ks, lane, out);
+        }
 #pragma unroll
         for (int gi = 0; gi < 2; ++gi) {
             const int rb = plan[wave][gi][0];
@@ -578,7 +758,7 @@ __global__ __launch_bounds__(kThreads, BF16 ? 3 : 2) void k1_prep_kernel(
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const int c = 32 * ks + 8 * q + e;
-                    const float fr = fast_exp2(sG[r][c] - sG[ref][c]);
+                    const float fr = fast_exp2(gdiff(r, ref, c));
                     X[ks][e] = (E)(kval(r, c) * fr);
                     Z[ks][e] = (E)(qf(qa[gi][ks][e]) * zq * fr);
                 }
@@ -588,6 +768,7 @@ __global__ __launch_bounds__(kThreads, BF16 ? 3 : 2) void k1_prep_kernel(
                 if (k2 >= plan[wave][gi][2]) break;
                 const int sb = plan[wave][gi][1] + k2;
                 const int s = 16 * sb + m;
+                if (sb == rb && ((slow_blocks >> rb) & 1u)) continue;  // after this loop
                 f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int ks = 0; ks < NKS; ++ks) {
@@ -595,28 +776,81 @@ __global__ __launch_bounds__(kThreads, BF16 ? 3 : 2) void k1_prep_kernel(
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
                         const int c = 32 * ks + 8 * q + e;
-                        Y[e] = (E)(kval(s, c) * fast_exp2(sG[ref][c] - sG[s][c]));
+                        Y[e] = (E)(kval(s, c) * fast_exp2(gdiff(ref, s, c)));
                     }
                     accA = M::run(X[ks], Y, accA);  // rows r, cols s
                     accP = M::run(Y, Z[ks], accP);  // P^T: rows s, cols r
                 }
-                // A[r'][s'] with r' = 16rb + 4q + i, s' = 16sb + m, kept in
-                // registers until every wave is done reading K
+                store_pair(gi, k2, rb, sb, accA, accP);
+            }
+        }
+        // Diagonal pairs whose block decays too much: done here, where the
+        // row-block operands and prefetched queries of the loop above are dead.
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int rr = 16 * rb + 4 * q + i, ss = 16 * sb + m;
-                    aT[2 * gi + k2][i] = ss < rr ? sB[rr] * accA[i] : 0.f;
-                }
-                // P^T[s'][r'] with s' = 16sb + 4q + i, r' = 16rb + m -> P A-frag
-                // [rt = rb][slab sb/2], slots 4*(sb%2) + i of lane (m + 16q).
-                typedef E e4 __attribute__((ext_vector_type(4)));
-                e4 pv;
+        for (int gi = 0; gi < 2; ++gi) {
+            const int rb = plan[wave][gi][0];
+            if (rb < 0) break;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int ss = 16 * sb + 4 * q + i, rr = 16 * rb + m;
-                    pv[i] = (E)(ss <= rr ? accP[i] : 0.f);
+            for (int k2 = 0; k2 < 2; ++k2) {
+                if (k2 >= plan[wave][gi][2]) break;
+                const int sb = plan[wave][gi][1] + k2;
+                if (sb != rb || !((slow_blocks >> rb) & 1u)) continue;
+                const int ref = 16 * rb;
+                const int r = 16 * rb + m;
+                const float zq = L2 ? sQn[r] : 1.f;
+                f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
+                // Four levels h = 8, 4, 2, 1 over the local row index
+                // (lane row m): rows with bit h set (r side) take
+                // e^(G_m - G_{m & ~(h-1)}), rows with bit h clear (s side)
+                // take e^(G_{(m & ~(h-1)) + h} - G_m); both are <= 1, and
+                // for r, s in one 2h-run on opposite sides of its middle
+                // their product is e^(G_r - G_s). Each level keeps only
+                // those pairs; P's diagonal (factor 1) is added at the end.
+                // The row's queries are read again (cache-hot) rather than
+                // kept live from the prefetch.
+                tin8 qs[NKS];
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks)
+                    qs[ks] = *reinterpret_cast<const tin8*>(row_ptr(Q, r) + 32 * ks + 8 * q);
+#pragma unroll 1
+                for (int lv = 0; lv < 4; ++lv) {
+                    const int hh = 8 >> lv;
+                    const bool up = (m & hh) != 0;
+                    const int oth = ref + (m & ~(hh - 1)) + (up ? 0 : hh);
+                    f32x4 tA = {0.f, 0.f, 0.f, 0.f}, tP = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ks = 0; ks < NKS; ++ks) {
+                        Frag Xl, Yl, Zl;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            const int c = 32 * ks + 8 * q + e;
+                            const float f = fast_exp2(up ? gdiff(r, oth, c) : gdiff(oth, r, c));
+                            const float kv = kval(r, c) * f;
+                            const float qv = qf(qs[ks][e]) * zq * f;
+                            Xl[e] = (E)(up ? kv : 0.f);
+                            Zl[e] = (E)(up ? qv : 0.f);
+                            Yl[e] = (E)(up ? 0.f : kv);
+                        }
+                        tA = M::run(Xl, Yl, tA);  // rows r, cols s
+                        tP = M::run(Yl, Zl, tP);  // P^T: rows s, cols r
+                    }
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int ra = 4 * q + i;  // A tile: row ra, column m
+                        accA[i] += (((ra ^ m) < 2 * hh) && (ra & hh) && !(m & hh)) ? tA[i] : 0.f;
+                        const int sp = 4 * q + i;  // P^T tile: row sp (s), column m (r)
+                        accP[i] += (((sp ^ m) < 2 * hh) && (m & hh) && !(sp & hh)) ? tP[i] : 0.f;
+                    }
                 }
-                *reinterpret_cast<e4*>(hb + HO::kP + ((size_t)(rb * 2 + sb / 2) * 64 + lane) * 8 + 4 * (sb % 2)) = pv;
+                float dq = 0.f;  // q_r . k_r over this lane's channels, then all four lanes of row m
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) dq += qf(qs[ks][e]) * kval(r, 32 * ks + 8 * q + e);
+                dq = pair_sum32(pair_sum16(dq)) * zq;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) accP[i] += (4 * q + i == m) ? dq : 0.f;
+                store_pair(gi, k2, rb, sb, accA, accP);
             }
         }
         // zero halves inside stored slabs: (rb, sb) = (0, 1) and (2, 3)
@@ -631,35 +865,19 @@ __global__ __launch_bounds__(kThreads, BF16 ? 3 : 2) void k1_prep_kernel(
             store_frag<Frag, E>(hb + HO::kP, wave * 2 + 1, lane, zf);
             store_frag<Frag, E>(hb + HO::kAb, wave * 2 + 1, lane, zf);
         }
-        // Qd A-frags: rows tokens (tile rt), K channels (slab ks, permuted)
-#pragma unroll
-        for (int i = 0; i < QDF; ++i) {
-            const int f = wave + 4 * i;
-            const int rt = f / NKS, ks = f % NKS;
-            const int r = 16 * rt + m;
-            // perm32(q, e): channels 32ks + 4q + e (e < 4) and 32ks + 16 + 4q + e - 4
-            Frag out;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int c = 32 * ks + perm32(q, e);
-                out[e] = (E)(qf(qd[i][e >> 2][e & 3]) * (L2 ? sQn[r] : 1.f) * fast_exp2(sG[r][c]));
-            }
-            store_frag<Frag, E>(hb + HO::kQd, rt * NKS + ks, lane, out);
-        }
         // Kc^T A-frags: rows channels (tile ct), K tokens (slab ts, permuted)
         for (int f = wave; f < NRT * 2; f += 4) {
             const int ct = f / 2, ts = f % 2;
             const int c = 16 * ct + m;
-            const float gl = sG[C - 1][c];
             Frag out;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int r = 32 * ts + perm32(q, e);
-                out[e] = (E)(kval(r, c) * fast_exp2(gl - sG[r][c]));
+                out[e] = (E)(kval(r, c) * fast_exp2(gdiff(C - 1, r, c)));
             }
             store_frag<Frag, E>(hb + HO::kKc, ct * 2 + ts, lane, out);
         }
-        for (int c = t; c < DK; c += kThreads) glast[c] = fast_exp2(sG[C - 1][c]);
+        for (int c = t; c < DK; c += kThreads) glast[c] = fast_exp2((float)sG[C - 1][c]);
     }
     // (beta Kd)^T operands of phase C, built while K is still in LDS:
     // row c = 16(2ks + half) + m, K index s = 32ts + 8q + e, ks = wave % NKS
@@ -674,7 +892,7 @@ __global__ __launch_bounds__(kThreads, BF16 ? 3 : 2) void k1_prep_kernel(
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const int s = 32 * ts + 8 * q + e;
-                    aF[half][ts][e] = (E)(sB[s] * kval(s, c) * fast_exp2(sG[s][c]));
+                    aF[half][ts][e] = (E)(sB[s] * kval(s, c) * fast_exp2((float)sG[s][c]));
                 }
             }
     }
@@ -1951,7 +2169,7 @@ __global__ __launch_bounds__(kThreads) void advance_chunk_kernel(
     __shared__ __attribute__((aligned(16))) float sG[C][KP];  // G * log2(e); rows >= r: G_{r-1}
     __shared__ __attribute__((aligned(16))) float sK[C][KP];  // keys (normalised with L2); rows >= r: 0
     __shared__ __attribute__((aligned(16))) float sS[DK][SP];  // S_n
-    __shared__ float sTot[NQ][DK];
+    __shared__ double sTot[NQ][DK];
 
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int q = lane >> 4, m = lane & 15;
@@ -1997,7 +2215,8 @@ __global__ __launch_bounds__(kThreads) void advance_chunk_kernel(
         *reinterpret_cast<f32x4*>(&sS[i / (WC / 4)][WC * half + 4 * (i % (WC / 4))]) = sreg[u];
     }
 
-    // ---- cumulative decay over rows < r (fp32, rows >= r add 0) and keys
+    // ---- cumulative decay over rows < r (rows >= r add 0) and keys: g
+    // floored and summed in fp64 as in K1, stored as fp32 G * log2(e)
     {
         const int c = t % DK, grp = t / DK;
         float gl[RPQ];
@@ -2006,19 +2225,19 @@ __global__ __launch_bounds__(kThreads) void advance_chunk_kernel(
             const int row = grp * RPQ + i;
             float x = row < r ? g[((t0 + row) * H + h) * DK + c] : 0.f;
             if ((front & kFrontGate) && row < r) x = -__expf(x);
-            gl[i] = x;
+            gl[i] = fmaxf(x, -kGFloorBF16);
         }
-        float acc = 0.f;
+        double acc = 0;
 #pragma unroll
-        for (int i = 0; i < RPQ; ++i) acc += gl[i];
+        for (int i = 0; i < RPQ; ++i) acc += (double)gl[i];
         sTot[grp][c] = acc;
         __syncthreads();
-        float run = 0.f;
+        double run = 0;
         for (int p = 0; p < grp; ++p) run += sTot[p][c];
 #pragma unroll
         for (int i = 0; i < RPQ; ++i) {
-            run += gl[i];
-            sG[grp * RPQ + i][c] = run * kLog2e;
+            run += (double)gl[i];
+            sG[grp * RPQ + i][c] = (float)(run * 1.4426950408889634);
         }
     }
     {  // keys: four threads per row, DK / 4 channels each, 16-byte loads
@@ -2179,10 +2398,15 @@ void launch_trio(const PrefillArgs& a, const Plan& p, int npairs, int cus, int l
     const int64_t wgs = (int64_t)npairs * NVB;
     const int64_t per_cu = (wgs + cus - 1) / cus;
     unsigned pad = 0;
-    hipFuncAttributes fa;
-    if (per_cu < 2 && hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(&k2_trio_kernel<DK, DV>)) == hipSuccess) {
+    // the kernel's static LDS, asked once per process
+    static const int64_t have = [] {
+        hipFuncAttributes fa;
+        return hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(&k2_trio_kernel<DK, DV>)) == hipSuccess
+                   ? (int64_t)fa.sharedSizeBytes
+                   : (int64_t)-1;
+    }();
+    if (per_cu < 2 && have >= 0) {
         const int64_t want = (int64_t)lds_max / per_cu - 512;
-        const int64_t have = (int64_t)fa.sharedSizeBytes;
         pad = want > have ? (unsigned)(want - have) : 0u;
     }
     hipLaunchKernelGGL((k2_trio_kernel<DK, DV>), dim3(grid), dim3(192), pad, stream,
@@ -2213,7 +2437,7 @@ hipError_t launch_typed(const PrefillArgs& a, hipStream_t stream) {
     const bool varlen = a.cu_seqlens != nullptr;
     const bool prepare = (a.phases & 1u) != 0, scan = (a.phases & 2u) != 0;
     if (prepare && varlen)
-        hipLaunchKernelGGL(prep_kernel, dim3(1), dim3(kThreads), 0, stream, a.cu_seqlens, a.num_seqs,
+        hipLaunchKernelGGL(prep_kernel, dim3(1), dim3(kPrepThreads), 0, stream, a.cu_seqlens, a.num_seqs,
                            a.total_tokens, a.ckpt_interval, p.chunk_start, p.ckpt_base, p.order);
     if (prepare && p.max_chunks > 0 && a.total_tokens > 0) {
         auto k1 = (a.frontend & kFrontL2) ? &k1_prep_kernel<DK, BF16, true>
@@ -2234,17 +2458,8 @@ hipError_t launch_typed(const PrefillArgs& a, hipStream_t stream) {
     // five-wave one, thousands the 64-column one. fp32 operands take the
     // four-wave kernel with 16 columns.
     const int npairs = a.num_seqs * a.H;
-    int cus = 256, lds_max = 65536;
-    {
-        int dev = 0;
-        if (hipGetDevice(&dev) == hipSuccess) {
-            int n = 0;
-            if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
-                cus = n;
-            if (hipDeviceGetAttribute(&n, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) == hipSuccess && n > 0)
-                lds_max = n;
-        }
-    }
+    const DeviceInfo di = device_info();
+    const int cus = di.cus, lds_max = di.lds_per_block;
     enum { kTrio, kQuad, kNt4, kNt1 } design = kNt1;
     if (BF16) {
         const int64_t blocks = (int64_t)npairs * (DV / 16);  // 16-column blocks

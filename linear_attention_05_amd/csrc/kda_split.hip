@@ -340,9 +340,9 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
                           a.ckpt_interval == 0 && a.pos.num_pos == 0 && a.total_tokens > 0;
     int P = 1;
     if (eligible) {
-        int cus = 0, dev = 0;
-        if (hipGetDevice(&dev) == hipSuccess &&
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess) {
+        const DeviceInfo di = device_info();
+        if (di.valid) {
+            const int cus = di.cus;
             const int want = prefill_split_segments(a.total_tokens, 1, a.H, a.Dk, a.Dv, cus);
             const int sized = prefill_split_segments(a.total_tokens, 1, a.H, a.Dk, a.Dv, kSizingCUs);
             // the workspace was sized for `sized` segments: never use more
