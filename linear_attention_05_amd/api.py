@@ -25,19 +25,34 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
-def _check(t, name, dtype=None, shape=None, device=None):
+def _check_props(t, name, dtype=None, shape=None):
+    """dtype, shape (None entries match any size) and contiguity."""
+    if t is None:
+        return
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None:
+        ok = t.dim() == len(shape) and all(w is None or int(n) == int(w)
+                                            for n, w in zip(t.shape, shape))
+        if not ok:
+            want = tuple("*" if w is None else w for w in shape)
+            raise ValueError(f"{name} must have shape {want}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _check_place(t, name, device):
     if t is None:
         return
     if not t.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor")
-    if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous")
-    if dtype is not None and t.dtype != dtype:
-        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
-    if shape is not None and tuple(t.shape) != tuple(shape):
-        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
     if device is not None and t.device != device:
         raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _check(t, name, dtype=None, shape=None, device=None):
+    _check_props(t, name, dtype, shape)
+    _check_place(t, name, device)
 
 
 def _stream(device):
@@ -103,37 +118,50 @@ def _prefill(q, k, v, g, beta, cu_seqlens, num_seqs, initial_state, output_final
              frontend, pos_offsets, pos_values, pos_states):
     """Argument checks, output allocation and the call of the matching entry point."""
     dev = q.device
+    if q.dim() != 3 or v.dim() != 3:
+        raise ValueError("q, k, v must be [tokens, heads, dim]")
     N, H, Dk = q.shape
     Dv = v.shape[-1]
     code = _dtype_code(q)
     if num_seqs is None:
         num_seqs = 1 if cu_seqlens is None else cu_seqlens.numel() - 1
-    _check(q, "q", q.dtype, (N, H, Dk), dev)
-    _check(k, "k", q.dtype, (N, H, Dk), dev)
-    _check(v, "v", q.dtype, (N, H, Dv), dev)
-    _check(g, "g", torch.float32, (N, H, Dk), dev)
-    _check(beta, "beta", torch.float32, (N, H), dev)
-    _check(cu_seqlens, "cu_seqlens", torch.int32, (num_seqs + 1,), dev)
-    _check(initial_state, "initial_state", torch.float32, (num_seqs, H, Dk, Dv), dev)
+    # every caller-supplied tensor's dtype and shape first (so that a wrong
+    # shape is reported before anything else), then where it lives
+    given = [(q, "q", q.dtype, (N, H, Dk)), (k, "k", q.dtype, (N, H, Dk)),
+             (v, "v", q.dtype, (N, H, Dv)), (g, "g", torch.float32, (N, H, Dk)),
+             (beta, "beta", torch.float32, (N, H)),
+             (cu_seqlens, "cu_seqlens", torch.int32, (num_seqs + 1,)),
+             (initial_state, "initial_state", torch.float32, (num_seqs, H, Dk, Dv)),
+             (o, "o", torch.float32, (N, H, Dv)),
+             (final_state, "final_state", torch.float32, (num_seqs, H, Dk, Dv)),
+             # the library writes rows [0, ckpt_states.shape[0]) of [rows, H, Dk, Dv]
+             (ckpt_states, "ckpt_states", torch.float32, (None, H, Dk, Dv)),
+             (workspace, "workspace", torch.uint8, None)]
+    if pos_offsets is not None or pos_values is not None:
+        if pos_offsets is None or pos_values is None:
+            raise ValueError("pos_offsets and pos_values go together")
+        npos = int(pos_values.numel())
+        given += [(pos_offsets, "pos_offsets", torch.int32, (num_seqs + 1,)),
+                  (pos_values, "pos_values", torch.int32, (npos,)),
+                  (pos_states, "pos_states", torch.float32, (npos, H, Dk, Dv))]
+    for t, name, dt, shape in given:
+        _check_props(t, name, dt, shape)
+    for t, name, _, _ in given:
+        _check_place(t, name, dev)
     if o is None:
         o = torch.empty((N, H, Dv), dtype=torch.float32, device=dev)
-    _check(o, "o", torch.float32, (N, H, Dv), dev)
     if final_state is None and output_final_state:
         final_state = torch.empty((num_seqs, H, Dk, Dv), dtype=torch.float32, device=dev)
-    _check(final_state, "final_state", torch.float32, (num_seqs, H, Dk, Dv), dev)
     if ckpt_interval > 0 and ckpt_states is None:
         if num_checkpoints is None:
             raise ValueError("ckpt_interval > 0 needs num_checkpoints or ckpt_states")
         ckpt_states = torch.empty((max(int(num_checkpoints), 0), H, Dk, Dv),
                                   dtype=torch.float32, device=dev)
-    if ckpt_states is not None:
-        _check(ckpt_states, "ckpt_states", torch.float32, None, dev)
     need = B.workspace_size(N, num_seqs, H, Dk, Dv, code, CHUNK)
     if need == 0:
         raise B.KdaError(B.KDA_ERR_UNSUPPORTED, "kda_prefill_workspace_size")
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    _check(workspace, "workspace", torch.uint8, None, dev)
     ck_ptr = _ptr(ckpt_states) if ckpt_interval > 0 else None
     ck_rows = int(ckpt_states.shape[0]) if ckpt_interval > 0 else 0
     if ckpt_interval > 0 and ckpt_states.numel() == 0:
@@ -144,12 +172,8 @@ def _prefill(q, k, v, g, beta, cu_seqlens, num_seqs, initial_state, output_final
             ck_rows, _ptr(o))
     tail = (_ptr(workspace), workspace.numel(), int(phases))
     if pos_offsets is not None:
-        _check(pos_offsets, "pos_offsets", torch.int32, (num_seqs + 1,), dev)
-        _check(pos_values, "pos_values", torch.int32, None, dev)
-        npos = int(pos_values.numel())
         if pos_states is None:
             pos_states = torch.empty((npos, H, Dk, Dv), dtype=torch.float32, device=dev)
-        _check(pos_states, "pos_states", torch.float32, (npos, H, Dk, Dv), dev)
         st = B.prefill_at_raw(*head, _ptr(pos_offsets), _ptr(pos_values), npos,
                               _ptr(pos_states), *tail, int(frontend), _stream(dev))
         where = "kda_prefill_chunked_at"

@@ -167,3 +167,29 @@ def test_binding_refuses_cpu_tensors():
     with pytest.raises(ValueError):
         K.kda_decode_step(x, x, x, torch.zeros(1, 1, 64), torch.zeros(1, 1),
                           torch.zeros(1, 1, 64, 64))
+
+
+def test_binding_rejects_wrong_checkpoint_and_position_shapes():
+    """The library writes checkpoint rows [0, rows) of a [rows, H, Dk, Dv]
+    buffer and reads one position per element of pos_values: a tensor of any
+    other shape is refused before any pointer reaches it (checked before the
+    device, so plain CPU tensors show it)."""
+    torch = pytest.importorskip("torch")
+    import linear_attention_05_amd as K
+    N, H, D = 128, 2, 64
+    q, k, v, g = (torch.zeros(N, H, D) for _ in range(4))
+    beta = torch.zeros(N, H)
+    for bad in (torch.zeros(2, H, D), torch.zeros(2, H + 1, D, D), torch.zeros(2 * H * D * D),
+                torch.zeros(2, H, D, D + 1), torch.zeros(2, H, D // 2, D)):
+        with pytest.raises(ValueError, match="ckpt_states"):
+            K.kda_prefill_chunked(q, k, v, g, beta, ckpt_interval=64, ckpt_states=bad)
+    offs = torch.zeros(2, dtype=torch.int32)
+    with pytest.raises(ValueError, match="pos_values"):
+        K.kda_prefill_chunked_at(q, k, v, g, beta, offs, torch.zeros(2, 2, dtype=torch.int32))
+    with pytest.raises(ValueError, match="pos_states"):
+        K.kda_prefill_chunked_at(q, k, v, g, beta, offs, torch.zeros(3, dtype=torch.int32),
+                                 pos_states=torch.zeros(2, H, D, D))
+    # shapes right, tensors on the CPU: refused for where they live
+    with pytest.raises(ValueError, match="GPU tensor"):
+        K.kda_prefill_chunked(q, k, v, g, beta, ckpt_interval=64,
+                              ckpt_states=torch.zeros(2, H, D, D))
