@@ -36,3 +36,28 @@ def assert_parity(got, ref, dtype, what=""):
     assert max_abs <= tol_abs and rel_f <= tol_rel, \
         f"{what}: max_abs {max_abs:.3e} (tol {tol_abs:g}), rel_F {rel_f:.3e} (tol {tol_rel:g})"
     return max_abs, rel_f
+
+
+def assert_parity_blocked(got, ref, dtype, what="", axis=1, block=4):
+    """assert_parity over the whole tensors, computed slice by slice along
+    `axis` (bounded temporaries for multi-GB outputs): the same max |diff| and
+    ||diff||_F / ||ref||_F as one pass would give."""
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    n = got.shape[axis]
+    max_abs, dd, rr = 0.0, 0.0, 0.0
+    for a in range(0, n, block):
+        idx = [slice(None)] * got.ndim
+        idx[axis] = slice(a, min(a + block, n))
+        g = np.asarray(got[tuple(idx)], dtype=np.float64)
+        r = np.asarray(ref[tuple(idx)], dtype=np.float64)
+        assert np.isfinite(g).all(), f"{what}: non-finite values in GPU output"
+        d = g - r
+        if d.size:
+            max_abs = max(max_abs, float(np.abs(d).max()))
+        dd += float(np.sum(d * d))
+        rr += float(np.sum(r * r))
+    rel_f = float(np.sqrt(dd / rr)) if rr > 0 else float(np.sqrt(dd))
+    tol_abs, tol_rel = TOL[dtype]
+    assert max_abs <= tol_abs and rel_f <= tol_rel, \
+        f"{what}: max_abs {max_abs:.3e} (tol {tol_abs:g}), rel_F {rel_f:.3e} (tol {tol_rel:g})"
+    return max_abs, rel_f

@@ -1,13 +1,12 @@
 """GPU parity of kda_prefill_chunked against the fp64 oracle (through the C ABI).
 
-Small problems are compared element by element on every output; the
-full-size workloads are compared on (sequence, head, 16-column) units that
-the oracle computes one by one, covering all tokens of those units."""
+Every problem, the full-size workloads included, is compared element by
+element on every output."""
 
 import numpy as np
 import pytest
 
-from helpers import assert_parity, dev_tensor, errors
+from helpers import assert_parity, assert_parity_blocked, dev_tensor, errors
 from oracle import recurrence
 from synth import make_prefill, make_workload, WORKLOADS
 
@@ -139,56 +138,37 @@ def test_prefill_matches_decode_steps():
     assert ma < 2e-3 and rf < 1e-3, (ma, rf)
 
 
-def _sampled_units(x, n_units, rng):
-    units = {(0, 0, 0), (x.num_seqs - 1, x.H - 1, x.Dv // 16 - 1)}
-    while len(units) < n_units:
-        units.add((int(rng.integers(x.num_seqs)), int(rng.integers(x.H)),
-                   int(rng.integers(x.Dv // 16))))
-    return np.array(sorted(units), dtype=np.int32)
-
-
-def check_sampled(x, n_units, seed):
+def check_workload(x):
+    """Every output element of a full-size workload against the oracle (the
+    oracle runs over all sequences, heads and columns; the comparison goes
+    head block by head block to bound host memory)."""
     print(f"prefill full-size {x.name}: tokens={x.total_tokens} seqs={x.num_seqs}", flush=True)
     o, fs, ck = gpu_prefill(x)
-    assert np.isfinite(o).all() and np.isfinite(fs).all()
-    units = _sampled_units(x, n_units, np.random.default_rng(seed))
-    r = recurrence.prefill(x.q, x.k, x.v, x.g, x.beta, x.cu_seqlens,
-                           initial_state=x.initial_state, ckpt_interval=x.ckpt_interval,
-                           units=units, col_block=16)
-    cu = x.cu_seqlens
-    go, ro, gf, rfin, gc, rc = [], [], [], [], [], []
-    nck = [0] + list(np.cumsum([L // x.ckpt_interval if x.ckpt_interval else 0 for L in x.lengths]))
-    for s, h, cb in units:
-        cols = slice(16 * cb, 16 * cb + 16)
-        go.append(o[cu[s]:cu[s + 1], h, cols].ravel())
-        ro.append(r["o"][cu[s]:cu[s + 1], h, cols].ravel())
-        gf.append(fs[s, h, :, cols].ravel())
-        rfin.append(r["final"][s, h, :, cols].ravel())
-        if x.ckpt_interval:
-            gc.append(ck[nck[s]:nck[s + 1], h, :, cols].ravel())
-            rc.append(r["ckpt"][nck[s]:nck[s + 1], h, :, cols].ravel())
-    res = {"o": assert_parity(np.concatenate(go), np.concatenate(ro), x.dtype, "o (sampled)"),
-           "final": assert_parity(np.concatenate(gf), np.concatenate(rfin), x.dtype, "final (sampled)")}
+    print("  gpu done; oracle over all outputs", flush=True)
+    r = oracle_full(x)
+    res = {"o": assert_parity_blocked(o, r["o"], x.dtype, "o", axis=1),
+           "final": assert_parity_blocked(fs, r["final"], x.dtype, "final", axis=1)}
     if x.ckpt_interval:
-        res["ckpt"] = assert_parity(np.concatenate(gc), np.concatenate(rc), x.dtype, "ckpt (sampled)")
+        assert ck.shape == r["ckpt"].shape
+        res["ckpt"] = assert_parity_blocked(ck, r["ckpt"], x.dtype, "checkpoints", axis=1)
     print(res, flush=True)
     return res
 
 
 def test_workload_prefill_8k():
-    check_sampled(make_workload(1), 12, 1)
+    check_workload(make_workload(1))
 
 
 def test_workload_long_context_checkpoints():
     x = make_workload(2)
     assert x.num_checkpoints() == 4
-    check_sampled(x, 4, 2)
+    check_workload(x)
 
 
 def test_workload_varlen_64_sequences():
     x = make_workload(3)
     assert x.num_seqs == 64 and min(x.lengths) >= 128 and max(x.lengths) <= 16384
-    check_sampled(x, 24, 3)
+    check_workload(x)
 
 
 def _with(x, **arrays):
@@ -234,6 +214,17 @@ def test_many_short_sequences():
     lengths = [int(v) for v in rng.integers(0, 71, size=600)]
     x = make_prefill(lengths, 2, 64, 64, "bf16", 45, init_state=True, ckpt_interval=64)
     check_full(x, "600 sequences")
+
+
+def test_twenty_thousand_short_sequences():
+    """20,000 sequences of 0..100 tokens (three tiles of the varlen prep
+    kernel's offset scans and length-class sort): every output against the
+    oracle; a sequence left out of, or counted twice in, the scan order would
+    leave its outputs and final state unwritten or wrong."""
+    rng = np.random.default_rng(48)
+    lengths = [int(v) for v in rng.integers(0, 101, size=20000)]
+    x = make_prefill(lengths, 1, 64, 64, "bf16", 49, init_state=True, ckpt_interval=64)
+    check_full(x, "20000 sequences")
 
 
 def test_long_tail_with_checkpoints():
