@@ -161,15 +161,21 @@ def bench_decode(steps, warmup):
     o = torch.empty(Bsz, H, D, device="cuda")
     for i in range(warmup):
         K.kda_decode_step(*inp[i % steps], state, o)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    # wall clock of back-to-back steps (no events between them) ...
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    for i in range(steps):
+        K.kda_decode_step(*inp[i], state, o)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    # ... and each step's kernel alone, between events
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    torch.cuda.synchronize()
     for i in range(steps):
         ev[i][0].record()
         K.kda_decode_step(*inp[i], state, o)
         ev[i][1].record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     per = [e[0].elapsed_time(e[1]) for e in ev]
     kern_ms = float(np.median(per))
     byts = Bsz * H * acc.decode_bytes_per_head_token(D, D, 2)
@@ -551,8 +557,20 @@ def main():
         mtok = p["n_tok"] / (step_ms * 1e-3) / 1e6
         k1 = roofline(p["k1_bytes"], p["k1_ms"], measured_traffic("k1_prep"))
         k2 = roofline(p["k2_bytes"], p["k2_ms"], measured_traffic("k2_scan"))
-        dominant, dom_name = (k2, "k2_scan") if p["k2_ms"] >= p["k1_ms"] else (k1, "k1_prep")
-        dominant = dict(dominant, kernel=dom_name)
+        # Headline roofline: the method's algorithmic (compulsory) bytes of one
+        # call over the dominant kernel's event-timed duration; beside it the
+        # same bytes over the whole call, and the two kernels' counter traffic
+        # against those bytes (above 1: the K1 -> K2 handoff's round trip).
+        dom_name, dom_ms = ("k2_scan", p["k2_ms"]) if p["k2_ms"] >= p["k1_ms"] else ("k1_prep", p["k1_ms"])
+        comp = p["compulsory_bytes"]
+        t1, t2 = measured_traffic("k1_prep"), measured_traffic("k2_scan")
+        path_traffic = t1 + t2 if (t1 is not None and t2 is not None) else None
+        dominant = dict(roofline(comp, dom_ms, measured_traffic(dom_name)), kernel=dom_name,
+                        algorithmic_bytes=comp, kernel_ms=round(dom_ms, 4),
+                        whole_call_frac=round(comp / (step_ms * 1e-3) / 8e12, 4),
+                        path_traffic=path_traffic,
+                        traffic_over_algorithmic=(round(path_traffic / comp, 3)
+                                                  if path_traffic is not None else None))
         out.update({
             "metric": "KDA prefill Mtok/s & TFLOP/s (H=32,D=128); decode state HBM GB/s vs peak",
             "value": round(mtok, 3), "unit": "Mtok/s", "n_gpus": 1, "steps": args.steps,
@@ -567,6 +585,7 @@ def main():
             "prefill": {
                 "event_ms_per_step": round(p["event_ms"], 4),
                 "tflops_algorithmic": round(p["flops"] / (step_ms * 1e-3) / 1e12, 2),
+                "tflops_frac_of_bf16_mfma_peak": round(p["flops"] / (step_ms * 1e-3) / 2.5e15, 4),
                 "flops_per_step": p["flops"],
                 "path_compulsory_bytes": p["compulsory_bytes"],
                 "path_roofline_frac": round(p["compulsory_bytes"] / (step_ms * 1e-3) / 8e12, 4),
