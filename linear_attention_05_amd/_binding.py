@@ -11,7 +11,9 @@ import ctypes
 import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libkda.so")
+# KDA_LIBRARY names another build of the same ABI (the CPU tests load the
+# host-sanitized build this way); default: the in-tree libkda.so
+LIB_PATH = os.environ.get("KDA_LIBRARY") or os.path.join(PKG, "libkda.so")
 
 KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_WORKSPACE, KDA_ERR_HIP = range(5)
 KDA_F32, KDA_BF16 = 0, 1

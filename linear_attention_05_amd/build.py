@@ -70,5 +70,54 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     return LIB
 
 
+SAN_DIR = os.path.join(PKG, "_build", "sanitized")
+SAN_LIB = os.path.join(SAN_DIR, "libkda_hostsan.so")
+
+
+def build_host_sanitized(verbose: bool = False, jobs: int = 8) -> str:
+    """The library with its host code (argument validation, workspace sizing,
+    launch set-up) built with AddressSanitizer and UndefinedBehaviorSanitizer,
+    for CPU tests of the C ABI; device code as in build(). Load it with the
+    matching sanitizer runtime preloaded. Rebuilt only when a source or header
+    is newer than it."""
+    cc = hipcc()
+    os.makedirs(SAN_DIR, exist_ok=True)
+    srcs = sources()
+    deps = srcs + [os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".h")] + \
+        [os.path.join(INCLUDE, f) for f in os.listdir(INCLUDE)] + [os.path.abspath(__file__)]
+    if os.path.exists(SAN_LIB) and os.path.getmtime(SAN_LIB) > max(os.path.getmtime(d) for d in deps):
+        return SAN_LIB
+    san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+    def compile_one(src):
+        obj = os.path.join(SAN_DIR, os.path.basename(src)[:-4] + ".o")
+        cmd = [cc, *common_flags(), "-g", *san, "-c", src, "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError(f"hipcc failed on {src}:\n{res.stdout}\n{res.stderr}")
+        return obj
+
+    with ThreadPoolExecutor(max(1, min(jobs, len(srcs)))) as ex:
+        objs = list(ex.map(compile_one, srcs))
+    cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-shared-libsan", *san,
+           "-o", SAN_LIB, *objs]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True, capture_output=not verbose)
+    return SAN_LIB
+
+
+def sanitizer_runtime() -> str:
+    """Path of the compiler's shared AddressSanitizer runtime (with UBSan)."""
+    out = subprocess.run([hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"],
+                         capture_output=True, text=True).stdout.strip()
+    if not out or not os.path.exists(out):
+        raise RuntimeError("shared AddressSanitizer runtime not found")
+    return out
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))

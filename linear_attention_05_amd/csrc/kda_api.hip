@@ -6,6 +6,7 @@
 #include "kda_internal.h"
 
 #include <atomic>
+#include <cstring>
 #include <mutex>
 
 namespace kda {
@@ -46,7 +47,18 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 
 bool supported_dim(int32_t d) { return d == 64 || d == 128; }
 
-bool valid_dtype(kda_dtype_t t) { return t == KDA_F32 || t == KDA_BF16; }
+// The bits of an enum argument, read without an enum-typed load: a C caller
+// may pass any int where the ABI names an enum, and C++ gives an enum object
+// holding a value outside its enumerators no defined value.
+template <typename E>
+int enum_bits(const E& e) {
+    static_assert(sizeof(E) == sizeof(int), "the C enums of kda.h are int-sized");
+    int v;
+    std::memcpy(&v, &e, sizeof v);
+    return v;
+}
+
+bool valid_dtype(int t) { return t == KDA_F32 || t == KDA_BF16; }
 
 constexpr uint32_t kFrontMask = KDA_FRONT_L2NORM_QK | KDA_FRONT_GATE | KDA_FRONT_BETA_SIGMOID;
 static_assert(KDA_FRONT_L2NORM_QK == kda::kFrontL2 && KDA_FRONT_GATE == kda::kFrontGate &&
@@ -55,8 +67,8 @@ static_assert(KDA_FRONT_L2NORM_QK == kda::kFrontL2 && KDA_FRONT_GATE == kda::kFr
 
 // Shared size checks of the prefill entry points (sizes only, no pointers).
 kda_status_t check_prefill_sizes(int64_t total_tokens, int32_t num_seqs, int32_t H, int32_t Dk,
-                                 int32_t Dv, int32_t chunk_size, kda_dtype_t in_dtype) {
-    if (total_tokens < 0 || num_seqs < 1 || H < 1 || Dk < 1 || Dv < 1 || !valid_dtype(in_dtype))
+                                 int32_t Dv, int32_t chunk_size, int dt) {
+    if (total_tokens < 0 || num_seqs < 1 || H < 1 || Dk < 1 || Dv < 1 || !valid_dtype(dt))
         return KDA_ERR_INVALID_ARG;
     if (total_tokens > (int64_t)INT32_MAX || (int64_t)num_seqs * H > (int64_t)INT32_MAX / 16)
         return KDA_ERR_UNSUPPORTED;
@@ -75,7 +87,7 @@ extern "C" {
 int kda_version(void) { return kVersion; }
 
 const char* kda_status_string(kda_status_t s) {
-    switch (s) {
+    switch (enum_bits(s)) {
         case KDA_OK: return "KDA_OK";
         case KDA_ERR_INVALID_ARG: return "KDA_ERR_INVALID_ARG: invalid argument";
         case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED: unsupported size or option";
@@ -87,9 +99,10 @@ const char* kda_status_string(kda_status_t s) {
 
 size_t kda_prefill_workspace_size(int64_t total_tokens, int32_t num_seqs, int32_t H, int32_t Dk,
                                   int32_t Dv, int32_t chunk_size, kda_dtype_t in_dtype) {
-    if (check_prefill_sizes(total_tokens, num_seqs, H, Dk, Dv, chunk_size, in_dtype) != KDA_OK)
+    const int dt = enum_bits(in_dtype);
+    if (check_prefill_sizes(total_tokens, num_seqs, H, Dk, Dv, chunk_size, dt) != KDA_OK)
         return 0;
-    const bool bf16 = in_dtype == KDA_BF16;
+    const bool bf16 = dt == KDA_BF16;
     const size_t plain = kda::prefill_workspace_bytes(total_tokens, num_seqs, H, Dk, Dv, bf16);
     const size_t split = kda::prefill_split_workspace_bytes(total_tokens, num_seqs, H, Dk, Dv, bf16);
     return plain > split ? plain : split;
@@ -97,7 +110,7 @@ size_t kda_prefill_workspace_size(int64_t total_tokens, int32_t num_seqs, int32_
 
 int32_t kda_prefill_scan_segments(int64_t total_tokens, int32_t num_seqs, int32_t H, int32_t Dk,
                                   int32_t Dv, int32_t chunk_size, kda_dtype_t in_dtype) {
-    if (check_prefill_sizes(total_tokens, num_seqs, H, Dk, Dv, chunk_size, in_dtype) != KDA_OK)
+    if (check_prefill_sizes(total_tokens, num_seqs, H, Dk, Dv, chunk_size, enum_bits(in_dtype)) != KDA_OK)
         return 0;
     const kda::DeviceInfo di = kda::device_info();
     if (!di.valid) return 1;
@@ -108,17 +121,21 @@ int32_t kda_prefill_scan_segments(int64_t total_tokens, int32_t num_seqs, int32_
     return P < 2 ? 1 : P;
 }
 
-kda_status_t kda_prefill_chunked_at(const void* q, const void* k, const void* v,
-                                    kda_dtype_t in_dtype, const float* g, const float* beta,
-                                    const int32_t* cu_seqlens, int32_t num_seqs,
-                                    int64_t total_tokens, int32_t H, int32_t Dk, int32_t Dv,
-                                    int32_t chunk_size, const float* initial_state,
-                                    float* final_state, int64_t ckpt_interval,
-                                    float* ckpt_states, int64_t ckpt_rows, float* o,
-                                    const int32_t* pos_offsets, const int32_t* pos_values,
-                                    int32_t num_pos, float* pos_states, void* workspace,
-                                    size_t workspace_bytes, uint32_t phases, uint32_t frontend,
-                                    hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation (host only, before any HIP call) and launch of every prefill
+// entry point.
+kda_status_t prefill_impl(const void* q, const void* k, const void* v, int dt,
+                          const float* g, const float* beta, const int32_t* cu_seqlens,
+                          int32_t num_seqs, int64_t total_tokens, int32_t H, int32_t Dk,
+                          int32_t Dv, int32_t chunk_size, const float* initial_state,
+                          float* final_state, int64_t ckpt_interval, float* ckpt_states,
+                          int64_t ckpt_rows, float* o, const int32_t* pos_offsets,
+                          const int32_t* pos_values, int32_t num_pos, float* pos_states,
+                          void* workspace, size_t workspace_bytes,
+                          uint32_t phases, uint32_t frontend, hipStream_t stream) {
     if (phases == 0 || (phases & ~(KDA_PHASE_PREPARE | KDA_PHASE_SCAN)) != 0)
         return KDA_ERR_INVALID_ARG;
     if (frontend & ~kFrontMask) return KDA_ERR_INVALID_ARG;
@@ -129,7 +146,7 @@ kda_status_t kda_prefill_chunked_at(const void* q, const void* k, const void* v,
             return KDA_ERR_INVALID_ARG;
         if ((int64_t)num_pos * H * 4 > (int64_t)INT32_MAX) return KDA_ERR_UNSUPPORTED;  // advance grid
     }
-    kda_status_t st = check_prefill_sizes(total_tokens, num_seqs, H, Dk, Dv, chunk_size, in_dtype);
+    kda_status_t st = check_prefill_sizes(total_tokens, num_seqs, H, Dk, Dv, chunk_size, dt);
     if (st != KDA_OK) return st;
     if (!cu_seqlens && num_seqs != 1) return KDA_ERR_INVALID_ARG;
     if (total_tokens > 0 && (!q || !k || !v || !g || !beta || !o)) return KDA_ERR_INVALID_ARG;
@@ -141,7 +158,7 @@ kda_status_t kda_prefill_chunked_at(const void* q, const void* k, const void* v,
     for (const void* p : ptrs)
         if (p && !aligned(p, 16)) return KDA_ERR_INVALID_ARG;
     const size_t need =
-        kda::prefill_workspace_bytes(total_tokens, num_seqs, H, Dk, Dv, in_dtype == KDA_BF16);
+        kda::prefill_workspace_bytes(total_tokens, num_seqs, H, Dk, Dv, dt == KDA_BF16);
     if (!workspace || workspace_bytes < need) return KDA_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return KDA_ERR_INVALID_ARG;
 
@@ -149,7 +166,7 @@ kda_status_t kda_prefill_chunked_at(const void* q, const void* k, const void* v,
     a.q = q;
     a.k = k;
     a.v = v;
-    a.bf16 = in_dtype == KDA_BF16;
+    a.bf16 = dt == KDA_BF16;
     a.g = g;
     a.beta = beta;
     a.cu_seqlens = cu_seqlens;
@@ -177,6 +194,27 @@ kda_status_t kda_prefill_chunked_at(const void* q, const void* k, const void* v,
     return kda::launch_prefill(a, stream) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
+}  // namespace
+
+extern "C" {
+
+kda_status_t kda_prefill_chunked_at(const void* q, const void* k, const void* v,
+                                    kda_dtype_t in_dtype, const float* g, const float* beta,
+                                    const int32_t* cu_seqlens, int32_t num_seqs,
+                                    int64_t total_tokens, int32_t H, int32_t Dk, int32_t Dv,
+                                    int32_t chunk_size, const float* initial_state,
+                                    float* final_state, int64_t ckpt_interval,
+                                    float* ckpt_states, int64_t ckpt_rows, float* o,
+                                    const int32_t* pos_offsets, const int32_t* pos_values,
+                                    int32_t num_pos, float* pos_states, void* workspace,
+                                    size_t workspace_bytes, uint32_t phases, uint32_t frontend,
+                                    hipStream_t stream) {
+    return prefill_impl(q, k, v, enum_bits(in_dtype), g, beta, cu_seqlens, num_seqs, total_tokens,
+                        H, Dk, Dv, chunk_size, initial_state, final_state, ckpt_interval,
+                        ckpt_states, ckpt_rows, o, pos_offsets, pos_values, num_pos, pos_states,
+                        workspace, workspace_bytes, phases, frontend, stream);
+}
+
 kda_status_t kda_prefill_chunked_ex(const void* q, const void* k, const void* v,
                                     kda_dtype_t in_dtype, const float* g, const float* beta,
                                     const int32_t* cu_seqlens, int32_t num_seqs,
@@ -186,10 +224,10 @@ kda_status_t kda_prefill_chunked_ex(const void* q, const void* k, const void* v,
                                     float* ckpt_states, int64_t ckpt_rows, float* o,
                                     void* workspace, size_t workspace_bytes, uint32_t phases,
                                     uint32_t frontend, hipStream_t stream) {
-    return kda_prefill_chunked_at(q, k, v, in_dtype, g, beta, cu_seqlens, num_seqs, total_tokens,
-                                  H, Dk, Dv, chunk_size, initial_state, final_state,
-                                  ckpt_interval, ckpt_states, ckpt_rows, o, nullptr, nullptr, 0,
-                                  nullptr, workspace, workspace_bytes, phases, frontend, stream);
+    return prefill_impl(q, k, v, enum_bits(in_dtype), g, beta, cu_seqlens, num_seqs, total_tokens,
+                        H, Dk, Dv, chunk_size, initial_state, final_state, ckpt_interval,
+                        ckpt_states, ckpt_rows, o, nullptr, nullptr, 0, nullptr, workspace,
+                        workspace_bytes, phases, frontend, stream);
 }
 
 kda_status_t kda_prefill_chunked_phases(const void* q, const void* k, const void* v,
@@ -201,10 +239,10 @@ kda_status_t kda_prefill_chunked_phases(const void* q, const void* k, const void
                                         float* ckpt_states, int64_t ckpt_rows, float* o,
                                         void* workspace, size_t workspace_bytes, uint32_t phases,
                                         hipStream_t stream) {
-    return kda_prefill_chunked_ex(q, k, v, in_dtype, g, beta, cu_seqlens, num_seqs, total_tokens,
-                                  H, Dk, Dv, chunk_size, initial_state, final_state,
-                                  ckpt_interval, ckpt_states, ckpt_rows, o, workspace,
-                                  workspace_bytes, phases, 0u, stream);
+    return prefill_impl(q, k, v, enum_bits(in_dtype), g, beta, cu_seqlens, num_seqs, total_tokens,
+                        H, Dk, Dv, chunk_size, initial_state, final_state, ckpt_interval,
+                        ckpt_states, ckpt_rows, o, nullptr, nullptr, 0, nullptr, workspace,
+                        workspace_bytes, phases, 0u, stream);
 }
 
 kda_status_t kda_prefill_chunked(const void* q, const void* k, const void* v,
@@ -215,19 +253,21 @@ kda_status_t kda_prefill_chunked(const void* q, const void* k, const void* v,
                                  float* final_state, int64_t ckpt_interval, float* ckpt_states,
                                  int64_t ckpt_rows, float* o, void* workspace,
                                  size_t workspace_bytes, hipStream_t stream) {
-    return kda_prefill_chunked_phases(q, k, v, in_dtype, g, beta, cu_seqlens, num_seqs,
-                                      total_tokens, H, Dk, Dv, chunk_size, initial_state,
-                                      final_state, ckpt_interval, ckpt_states, ckpt_rows, o,
-                                      workspace, workspace_bytes,
-                                      KDA_PHASE_PREPARE | KDA_PHASE_SCAN, stream);
+    return prefill_impl(q, k, v, enum_bits(in_dtype), g, beta, cu_seqlens, num_seqs, total_tokens,
+                        H, Dk, Dv, chunk_size, initial_state, final_state, ckpt_interval,
+                        ckpt_states, ckpt_rows, o, nullptr, nullptr, 0, nullptr, workspace,
+                        workspace_bytes, KDA_PHASE_PREPARE | KDA_PHASE_SCAN, 0u, stream);
 }
 
-kda_status_t kda_decode_step_ex(const void* q, const void* k, const void* v,
-                                kda_dtype_t in_dtype, const float* g, const float* beta,
-                                int32_t B, int32_t H, int32_t Dk, int32_t Dv, float* state,
-                                float* o, uint32_t frontend, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+kda_status_t decode_impl(const void* q, const void* k, const void* v, int dt, const float* g,
+                         const float* beta, int32_t B, int32_t H, int32_t Dk, int32_t Dv,
+                         float* state, float* o, uint32_t frontend, hipStream_t stream) {
     if (frontend & ~kFrontMask) return KDA_ERR_INVALID_ARG;
-    if (B < 0 || H < 1 || Dk < 1 || Dv < 1 || !valid_dtype(in_dtype)) return KDA_ERR_INVALID_ARG;
+    if (B < 0 || H < 1 || Dk < 1 || Dv < 1 || !valid_dtype(dt)) return KDA_ERR_INVALID_ARG;
     if (!supported_dim(Dk) || !supported_dim(Dv)) return KDA_ERR_UNSUPPORTED;
     if ((int64_t)B * H > (int64_t)INT32_MAX) return KDA_ERR_UNSUPPORTED;
     if (B == 0) return KDA_OK;
@@ -235,16 +275,28 @@ kda_status_t kda_decode_step_ex(const void* q, const void* k, const void* v,
     const void* ptrs[] = {q, k, v, g, beta, state, o};
     for (const void* p : ptrs)
         if (!aligned(p, 16)) return KDA_ERR_INVALID_ARG;
-    return kda::launch_decode(q, k, v, in_dtype == KDA_BF16, g, beta, B, H, Dk, Dv, state, o,
+    return kda::launch_decode(q, k, v, dt == KDA_BF16, g, beta, B, H, Dk, Dv, state, o,
                               frontend, stream) == hipSuccess
                ? KDA_OK
                : KDA_ERR_HIP;
 }
 
+}  // namespace
+
+extern "C" {
+
+kda_status_t kda_decode_step_ex(const void* q, const void* k, const void* v,
+                                kda_dtype_t in_dtype, const float* g, const float* beta,
+                                int32_t B, int32_t H, int32_t Dk, int32_t Dv, float* state,
+                                float* o, uint32_t frontend, hipStream_t stream) {
+    return decode_impl(q, k, v, enum_bits(in_dtype), g, beta, B, H, Dk, Dv, state, o, frontend,
+                       stream);
+}
+
 kda_status_t kda_decode_step(const void* q, const void* k, const void* v, kda_dtype_t in_dtype,
                              const float* g, const float* beta, int32_t B, int32_t H, int32_t Dk,
                              int32_t Dv, float* state, float* o, hipStream_t stream) {
-    return kda_decode_step_ex(q, k, v, in_dtype, g, beta, B, H, Dk, Dv, state, o, 0u, stream);
+    return decode_impl(q, k, v, enum_bits(in_dtype), g, beta, B, H, Dk, Dv, state, o, 0u, stream);
 }
 
 }  // extern "C"

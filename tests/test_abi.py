@@ -193,3 +193,4 @@ def test_binding_rejects_wrong_checkpoint_and_position_shapes():
     with pytest.raises(ValueError, match="GPU tensor"):
         K.kda_prefill_chunked(q, k, v, g, beta, ckpt_interval=64,
                               ckpt_states=torch.zeros(2, H, D, D))
+
