@@ -277,6 +277,29 @@ kda_status_t kda_prefill_chunked_at(
     uint32_t frontend, hipStream_t stream);
 
 /*
+ * kda_prefill_chunked without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation). Its scratch is a fixed 128 MiB device
+ * array inside the library (one per device, held until the process ends,
+ * never allocated or freed by this call). Sizes whose
+ * kda_prefill_workspace_size-style need exceeds it are refused with
+ * KDA_ERR_WORKSPACE before any launch: with bf16 q/k/v, H = 32 and
+ * Dk = Dv = 128 that allows one sequence of up to 3,968 tokens. Every call on
+ * a device shares that device's array: calls that overlap in time on one
+ * device (different streams or threads) race and give undefined results. The
+ * array keeps the last call's contents, which no later call reads. Other
+ * arguments and results as kda_prefill_chunked; KDA_ERR_HIP if the array's
+ * address cannot be obtained.
+ */
+kda_status_t kda_prefill_chunked_noalloc(
+    const void *q, const void *k, const void *v, kda_dtype_t in_dtype,
+    const float *g, const float *beta, const int32_t *cu_seqlens,
+    int32_t num_seqs, int64_t total_tokens, int32_t H, int32_t Dk, int32_t Dv,
+    int32_t chunk_size, const float *initial_state, float *final_state,
+    int64_t ckpt_interval, float *ckpt_states, int64_t ckpt_rows, float *o,
+    hipStream_t stream);
+
+/*
  * One KDA decode step for B independent sequences (one new token each).
  *
  * For each (b, h): S <- (I - beta k k^T) Diag(exp(g)) S + beta k v^T and

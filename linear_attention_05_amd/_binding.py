@@ -22,7 +22,7 @@ KDA_F32, KDA_BF16 = 0, 1
 EXPORTS = ("kda_version", "kda_status_string", "kda_prefill_workspace_size",
            "kda_prefill_scan_segments",
            "kda_prefill_chunked", "kda_prefill_chunked_phases", "kda_prefill_chunked_ex",
-           "kda_prefill_chunked_at",
+           "kda_prefill_chunked_at", "kda_prefill_chunked_noalloc",
            "kda_decode_step", "kda_decode_step_ex")
 PHASE_PREPARE, PHASE_SCAN = 1, 2
 # KDA_FRONT_* bits of include/kda.h
@@ -70,6 +70,8 @@ def load():
     lib.kda_prefill_chunked_at.argtypes = list(lib.kda_prefill_chunked.argtypes[:19]) + [
         P, P, I32, P, P, SZ, ctypes.c_uint32, ctypes.c_uint32, P]
     lib.kda_prefill_chunked_at.restype = ctypes.c_int
+    lib.kda_prefill_chunked_noalloc.argtypes = list(lib.kda_prefill_chunked.argtypes[:19]) + [P]
+    lib.kda_prefill_chunked_noalloc.restype = ctypes.c_int
     lib.kda_decode_step.argtypes = [P, P, P, ctypes.c_int, P, P, I32, I32, I32, I32, P, P, P]
     lib.kda_decode_step.restype = ctypes.c_int
     lib.kda_decode_step_ex.argtypes = list(lib.kda_decode_step.argtypes[:-1]) + [
@@ -106,6 +108,17 @@ def prefill_raw(q, k, v, dtype_code, g, beta, cu_seqlens, num_seqs, total_tokens
                                       total_tokens, H, Dk, Dv, chunk_size, initial_state,
                                       final_state, ckpt_interval, ckpt_states, ckpt_rows, o,
                                       workspace, workspace_bytes, stream)
+
+
+def prefill_noalloc_raw(q, k, v, dtype_code, g, beta, cu_seqlens, num_seqs, total_tokens, H, Dk,
+                        Dv, chunk_size, initial_state, final_state, ckpt_interval, ckpt_states,
+                        ckpt_rows, o, stream) -> int:
+    """Direct call of kda_prefill_chunked_noalloc (the library's static scratch
+    instead of a workspace); returns the status."""
+    return load().kda_prefill_chunked_noalloc(q, k, v, dtype_code, g, beta, cu_seqlens, num_seqs,
+                                              total_tokens, H, Dk, Dv, chunk_size, initial_state,
+                                              final_state, ckpt_interval, ckpt_states, ckpt_rows,
+                                              o, stream)
 
 
 def prefill_phases_raw(q, k, v, dtype_code, g, beta, cu_seqlens, num_seqs, total_tokens, H, Dk,

@@ -37,6 +37,36 @@ DeviceInfo device_info() {
     return info[dev];
 }
 
+// ---- scratch of the allocation-free prefill entry point ----------------
+// The workspace of kda_prefill_chunked_noalloc: a fixed device array of the
+// library's code object (each device holds its own copy until the process
+// ends). Host code never uses its name as an address: the device address comes
+// from hipGetSymbolAddress, once per device, with that device current.
+constexpr size_t kScratchBytes = (size_t)128 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::atomic<bool> g_scratch_ready[kMaxScratchDevices];
+void* g_scratch_ptr[kMaxScratchDevices];
+std::mutex g_scratch_mu;
+}  // namespace
+
+// Device address of the current device's scratch (nullptr on failure).
+void* scratch_address() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) return nullptr;
+    if (g_scratch_ready[dev].load(std::memory_order_acquire)) return g_scratch_ptr[dev];
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ready[dev].load(std::memory_order_relaxed)) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return nullptr;
+        g_scratch_ptr[dev] = ptr;
+        g_scratch_ready[dev].store(true, std::memory_order_release);
+    }
+    return g_scratch_ptr[dev];
+}
+
 }  // namespace kda
 
 namespace {
@@ -126,7 +156,8 @@ int32_t kda_prefill_scan_segments(int64_t total_tokens, int32_t num_seqs, int32_
 namespace {
 
 // Validation (host only, before any HIP call) and launch of every prefill
-// entry point.
+// entry point. use_scratch: the workspace is the library's static scratch,
+// looked up only after every argument has passed.
 kda_status_t prefill_impl(const void* q, const void* k, const void* v, int dt,
                           const float* g, const float* beta, const int32_t* cu_seqlens,
                           int32_t num_seqs, int64_t total_tokens, int32_t H, int32_t Dk,
@@ -134,7 +165,7 @@ kda_status_t prefill_impl(const void* q, const void* k, const void* v, int dt,
                           float* final_state, int64_t ckpt_interval, float* ckpt_states,
                           int64_t ckpt_rows, float* o, const int32_t* pos_offsets,
                           const int32_t* pos_values, int32_t num_pos, float* pos_states,
-                          void* workspace, size_t workspace_bytes,
+                          void* workspace, size_t workspace_bytes, bool use_scratch,
                           uint32_t phases, uint32_t frontend, hipStream_t stream) {
     if (phases == 0 || (phases & ~(KDA_PHASE_PREPARE | KDA_PHASE_SCAN)) != 0)
         return KDA_ERR_INVALID_ARG;
@@ -159,6 +190,12 @@ kda_status_t prefill_impl(const void* q, const void* k, const void* v, int dt,
         if (p && !aligned(p, 16)) return KDA_ERR_INVALID_ARG;
     const size_t need =
         kda::prefill_workspace_bytes(total_tokens, num_seqs, H, Dk, Dv, dt == KDA_BF16);
+    if (use_scratch) {
+        if (need > kda::kScratchBytes) return KDA_ERR_WORKSPACE;
+        workspace = kda::scratch_address();  // the first HIP call
+        workspace_bytes = kda::kScratchBytes;
+        if (!workspace) return KDA_ERR_HIP;
+    }
     if (!workspace || workspace_bytes < need) return KDA_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return KDA_ERR_INVALID_ARG;
 
@@ -212,7 +249,7 @@ kda_status_t kda_prefill_chunked_at(const void* q, const void* k, const void* v,
     return prefill_impl(q, k, v, enum_bits(in_dtype), g, beta, cu_seqlens, num_seqs, total_tokens,
                         H, Dk, Dv, chunk_size, initial_state, final_state, ckpt_interval,
                         ckpt_states, ckpt_rows, o, pos_offsets, pos_values, num_pos, pos_states,
-                        workspace, workspace_bytes, phases, frontend, stream);
+                        workspace, workspace_bytes, false, phases, frontend, stream);
 }
 
 kda_status_t kda_prefill_chunked_ex(const void* q, const void* k, const void* v,
@@ -227,7 +264,7 @@ kda_status_t kda_prefill_chunked_ex(const void* q, const void* k, const void* v,
     return prefill_impl(q, k, v, enum_bits(in_dtype), g, beta, cu_seqlens, num_seqs, total_tokens,
                         H, Dk, Dv, chunk_size, initial_state, final_state, ckpt_interval,
                         ckpt_states, ckpt_rows, o, nullptr, nullptr, 0, nullptr, workspace,
-                        workspace_bytes, phases, frontend, stream);
+                        workspace_bytes, false, phases, frontend, stream);
 }
 
 kda_status_t kda_prefill_chunked_phases(const void* q, const void* k, const void* v,
@@ -242,7 +279,7 @@ kda_status_t kda_prefill_chunked_phases(const void* q, const void* k, const void
     return prefill_impl(q, k, v, enum_bits(in_dtype), g, beta, cu_seqlens, num_seqs, total_tokens,
                         H, Dk, Dv, chunk_size, initial_state, final_state, ckpt_interval,
                         ckpt_states, ckpt_rows, o, nullptr, nullptr, 0, nullptr, workspace,
-                        workspace_bytes, phases, 0u, stream);
+                        workspace_bytes, false, phases, 0u, stream);
 }
 
 kda_status_t kda_prefill_chunked(const void* q, const void* k, const void* v,
@@ -256,7 +293,21 @@ kda_status_t kda_prefill_chunked(const void* q, const void* k, const void* v,
     return prefill_impl(q, k, v, enum_bits(in_dtype), g, beta, cu_seqlens, num_seqs, total_tokens,
                         H, Dk, Dv, chunk_size, initial_state, final_state, ckpt_interval,
                         ckpt_states, ckpt_rows, o, nullptr, nullptr, 0, nullptr, workspace,
-                        workspace_bytes, KDA_PHASE_PREPARE | KDA_PHASE_SCAN, 0u, stream);
+                        workspace_bytes, false, KDA_PHASE_PREPARE | KDA_PHASE_SCAN, 0u, stream);
+}
+
+kda_status_t kda_prefill_chunked_noalloc(const void* q, const void* k, const void* v,
+                                         kda_dtype_t in_dtype, const float* g, const float* beta,
+                                         const int32_t* cu_seqlens, int32_t num_seqs,
+                                         int64_t total_tokens, int32_t H, int32_t Dk, int32_t Dv,
+                                         int32_t chunk_size, const float* initial_state,
+                                         float* final_state, int64_t ckpt_interval,
+                                         float* ckpt_states, int64_t ckpt_rows, float* o,
+                                         hipStream_t stream) {
+    return prefill_impl(q, k, v, enum_bits(in_dtype), g, beta, cu_seqlens, num_seqs, total_tokens,
+                        H, Dk, Dv, chunk_size, initial_state, final_state, ckpt_interval,
+                        ckpt_states, ckpt_rows, o, nullptr, nullptr, 0, nullptr, nullptr, 0, true,
+                        KDA_PHASE_PREPARE | KDA_PHASE_SCAN, 0u, stream);
 }
 
 }  // extern "C"

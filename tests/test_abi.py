@@ -194,3 +194,28 @@ def test_binding_rejects_wrong_checkpoint_and_position_shapes():
         K.kda_prefill_chunked(q, k, v, g, beta, ckpt_interval=64,
                               ckpt_states=torch.zeros(2, H, D, D))
 
+
+def prefill_noalloc(**kw):
+    a = dict(q=A, k=A, v=A, dt=B.KDA_BF16, g=A, beta=A, cu=None, S=1, N=256, H=2, Dk=128,
+             Dv=128, chunk=64, s0=None, sf=A, ci=0, ck=None, ckr=0, o=A, stream=None)
+    a.update(kw)
+    return B.prefill_noalloc_raw(a["q"], a["k"], a["v"], a["dt"], a["g"], a["beta"], a["cu"],
+                                 a["S"], a["N"], a["H"], a["Dk"], a["Dv"], a["chunk"], a["s0"],
+                                 a["sf"], a["ci"], a["ck"], a["ckr"], a["o"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), INV), (dict(o=None), INV), (dict(N=-1), INV), (dict(Dk=96), UNS),
+    (dict(S=2), INV), (dict(ci=96), UNS), (dict(v=A + 2), INV),
+    # more scratch than the library's fixed 128 MiB: refused, nothing launched
+    (dict(N=4032, H=32), WS), (dict(N=1 << 20, H=32), WS),
+])
+def test_prefill_noalloc_validation(kw, status):
+    """Every refusal happens before any HIP call (these run without a GPU)."""
+    assert prefill_noalloc(**kw) == status
+
+
+def test_noalloc_limit_is_the_stated_one():
+    """The stated limit: one sequence of 3,968 tokens fits at H = 32, D = 128,
+    bf16 (its workspace need is at most 128 MiB); 4,032 does not."""
+    assert ws_size(N=3968) <= 128 << 20 < ws_size(N=4032)

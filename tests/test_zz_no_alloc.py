@@ -1,0 +1,89 @@
+"""GPU test of kda_prefill_chunked_noalloc (the prefill with the library's
+static scratch instead of a caller workspace), through the C ABI: two calls in
+a row, the second on a smaller input, each against kda_prefill_chunked on the
+same inputs (identical kernels: the results must agree bit for bit) and
+against the oracle's tolerance."""
+
+import numpy as np
+import pytest
+
+from helpers import assert_parity, dev_tensor
+from oracle import recurrence
+from synth import make_prefill
+
+pytestmark = pytest.mark.gpu
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def run_noalloc(x):
+    import torch
+    from linear_attention_05_amd import _binding as B
+    dt = B.KDA_BF16 if x.dtype == "bf16" else B.KDA_F32
+    q, k, v, g, beta = (dev_tensor(a) for a in (x.q, x.k, x.v, x.g, x.beta))
+    cu = dev_tensor(x.cu_seqlens)
+    s0 = dev_tensor(x.initial_state) if x.initial_state is not None else None
+    o = torch.empty(x.total_tokens, x.H, x.Dv, device="cuda")
+    fs = torch.empty(x.num_seqs, x.H, x.Dk, x.Dv, device="cuda")
+    nck = x.num_checkpoints()
+    ck = torch.empty(max(nck, 1), x.H, x.Dk, x.Dv, device="cuda") if x.ckpt_interval else None
+    torch.cuda.synchronize()
+    st = B.prefill_noalloc_raw(_ptr(q), _ptr(k), _ptr(v), dt, _ptr(g), _ptr(beta), _ptr(cu),
+                               x.num_seqs, x.total_tokens, x.H, x.Dk, x.Dv, 64, _ptr(s0),
+                               _ptr(fs), x.ckpt_interval, _ptr(ck), nck if ck is not None else 0,
+                               _ptr(o), torch.cuda.current_stream().cuda_stream)
+    assert st == B.KDA_OK, B.status_string(st)
+    torch.cuda.synchronize()
+    return (o.cpu().numpy(), fs.cpu().numpy(),
+            None if ck is None else ck[:nck].cpu().numpy())
+
+
+def run_workspace(x):
+    import torch
+    import linear_attention_05_amd as K
+    s0 = dev_tensor(x.initial_state) if x.initial_state is not None else None
+    o, fs, ck = K.kda_prefill_chunked(
+        dev_tensor(x.q), dev_tensor(x.k), dev_tensor(x.v), dev_tensor(x.g), dev_tensor(x.beta),
+        cu_seqlens=dev_tensor(x.cu_seqlens), initial_state=s0, ckpt_interval=x.ckpt_interval,
+        num_checkpoints=x.num_checkpoints())
+    torch.cuda.synchronize()
+    return o.cpu().numpy(), fs.cpu().numpy(), None if ck is None else ck.cpu().numpy()
+
+
+def check(x, what):
+    print(f"noalloc {what}: lengths={x.lengths[:6]} H={x.H} Dk={x.Dk} Dv={x.Dv} {x.dtype}",
+          flush=True)
+    got = run_noalloc(x)
+    ref = run_workspace(x)
+    for a, b, name in zip(got, ref, ("o", "final", "ckpt")):
+        if a is None:
+            assert b is None
+            continue
+        assert_parity(a, b, x.dtype, f"{what} {name} vs workspace entry point")
+        assert np.array_equal(a, b), f"{what} {name}: differs from the workspace entry point"
+    r = recurrence.prefill(x.q, x.k, x.v, x.g, x.beta, x.cu_seqlens,
+                           initial_state=x.initial_state, ckpt_interval=x.ckpt_interval)
+    assert_parity(got[0], r["o"], x.dtype, f"{what} o vs oracle")
+    assert_parity(got[1], r["final"], x.dtype, f"{what} final vs oracle")
+
+
+def test_noalloc_two_calls_second_smaller():
+    # the largest size the scratch holds (one sequence of 3968 tokens, 32 heads,
+    # D = 128, bf16), then a smaller varlen batch with checkpoints
+    check(make_prefill([3968], 32, 128, 128, "bf16", 960, init_state=True), "max size")
+    check(make_prefill([300, 0, 129, 64], 4, 128, 128, "bf16", 961, init_state=True,
+                       ckpt_interval=64), "smaller varlen")
+
+
+def test_noalloc_fp32_then_smaller():
+    check(make_prefill([500, 77], 2, 64, 64, "f32", 962, init_state=True), "fp32")
+    check(make_prefill([65], 2, 64, 64, "f32", 963, init_state=False), "fp32 smaller")
+
+
+def test_noalloc_refuses_more_than_its_scratch():
+    from linear_attention_05_amd import _binding as B
+    st = B.prefill_noalloc_raw(1 << 20, 1 << 20, 1 << 20, B.KDA_BF16, 1 << 20, 1 << 20, None, 1,
+                               4032, 32, 128, 128, 64, None, 1 << 20, 0, None, 0, 1 << 20, None)
+    assert st == B.KDA_ERR_WORKSPACE
