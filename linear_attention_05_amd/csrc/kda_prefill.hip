@@ -1728,8 +1728,8 @@ __global__ __launch_bounds__(192) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 // every wave drains its prologue loads before its loop and issues each
 // loop's loads in a fixed order; the V and handoff pointers are not
 // __restrict__, which keeps prefetches from moving across the barriers.
-template <int DK, int DV>
-__global__ __launch_bounds__(320) __attribute__((amdgpu_waves_per_eu(1, 2))) void k2_quad_kernel(
+template <int DK, int DV, int NCB>
+__global__ __launch_bounds__(64 * (NCB + 3)) __attribute__((amdgpu_waves_per_eu(1, 2))) void k2_quad_kernel(
     const void* vin, const int32_t* __restrict__ cu, const int32_t* __restrict__ order,
     const int32_t* __restrict__ chunk_start, const int32_t* __restrict__ ckpt_base, int npairs,
     int64_t N, int H, int64_t max_chunks, const unsigned char* handoff,
@@ -1745,7 +1745,6 @@ __global__ __launch_bounds__(320) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
     constexpr int NST = DK / 16;    // state row tiles
     constexpr int NRT = C / 16;     // token row tiles
     constexpr int NVB = DV / 16;    // column blocks per (seq, head)
-    constexpr int NCB = 2;          // column blocks per workgroup
     constexpr int NWG = NVB / NCB;  // workgroups per (seq, head)
     constexpr int LPR = 2 * NCB;    // prep: lanes per V row segment (16 bytes each)
     constexpr int RPI = 64 / LPR;   // prep: V rows per load instruction
@@ -2418,13 +2417,13 @@ void launch_trio(const PrefillArgs& a, const Plan& p, int npairs, int cus, int l
 
 // Five-wave scan: one workgroup per (pair, 32 columns), one per CU (its LDS
 // use, about 150 KB, keeps a second one off the CU).
-template <int DK, int DV>
+template <int DK, int DV, int NCB>
 void launch_quad(const PrefillArgs& a, const Plan& p, int npairs, hipStream_t stream) {
-    constexpr int NWG = DV / 32;
+    constexpr int NWG = DV / (16 * NCB);
     const bool varlen = a.cu_seqlens != nullptr;
     const int64_t groups = (npairs + 7) / 8;
     const unsigned grid = (unsigned)(groups * 8 * NWG);
-    hipLaunchKernelGGL((k2_quad_kernel<DK, DV>), dim3(grid), dim3(320), 0, stream,
+    hipLaunchKernelGGL((k2_quad_kernel<DK, DV, NCB>), dim3(grid), dim3(64 * (NCB + 3)), 0, stream,
                        a.v, a.cu_seqlens, varlen ? p.order : nullptr,
                        varlen ? p.chunk_start : nullptr, varlen ? p.ckpt_base : nullptr, npairs,
                        a.total_tokens, a.H, p.max_chunks, p.handoff, a.initial_state, a.final_state,
@@ -2471,7 +2470,7 @@ hipError_t launch_typed(const PrefillArgs& a, hipStream_t stream) {
     if (scan) {
         switch (design) {
             case kTrio: launch_trio<DK, DV>(a, p, npairs, cus, lds_max, stream); break;
-            case kQuad: launch_quad<DK, DV>(a, p, npairs, stream); break;
+            case kQuad: launch_quad<DK, DV, 2>(a, p, npairs, stream); break;
             case kNt4: launch_scan<DK, DV, 4, BF16>(a, p, npairs, stream); break;
             default: launch_scan<DK, DV, 1, BF16>(a, p, npairs, stream); break;
         }
