@@ -508,7 +508,9 @@ __global__ __launch_bounds__(kThreads, BF16 ? 3 : (DK == 128 ? 1 : 2)) void k1_p
 
     const int t = threadIdx.x;
     const int lane = t & 63;
-    const int wave = t >> 6;
+    // wave-uniform (in a scalar register): branches and plan lookups on it
+    // stay scalar
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int q = lane >> 4;
     const int m = lane & 15;
     const TIn* K = static_cast<const TIn*>(kin);
@@ -557,14 +559,20 @@ __global__ __launch_bounds__(kThreads, BF16 ? 3 : (DK == 128 ? 1 : 2)) void k1_p
     //   qa[gi][ks]: row 16*rb + m, channels 32ks + 8q .. +7
     typedef TIn tin8 __attribute__((ext_vector_type(8)));
     typedef TIn tin4 __attribute__((ext_vector_type(4)));
-    const int plan[4][2][3] = {{{3, 0, 2}, {0, 0, 1}},   // {rb, sb_first, count}
-                               {{3, 2, 2}, {1, 0, 1}},
-                               {{2, 0, 2}, {-1, 0, 0}},
-                               {{2, 2, 1}, {1, 1, 1}}};
+    // Block pairs of phase A: group gi of a wave takes row block rb (-1: no
+    // group) with column blocks sb .. sb + count - 1:
+    //   wave 0: rb 3 with sb 0-1, rb 0 with sb 0    wave 1: rb 3 with sb 2-3, rb 1 with sb 0
+    //   wave 2: rb 2 with sb 0-1                     wave 3: rb 2 with sb 2,   rb 1 with sb 1
+    // One nibble per wave in a constant (F: -1), read with the uniform wave
+    // index, so no table sits in memory.
+    auto nib = [&](unsigned k) { const int v = (int)((k >> (4 * wave)) & 15u); return v == 15 ? -1 : v; };
+    auto plan_rb = [&](int gi) { return nib(gi == 0 ? 0x2233u : 0x1F10u); };
+    auto plan_sb = [&](int gi) { return nib(gi == 0 ? 0x2020u : 0x1000u); };
+    auto plan_cnt = [&](int gi) { return nib(gi == 0 ? 0x1222u : 0x1011u); };
     tin8 qa[2][NKS];
 #pragma unroll
     for (int gi = 0; gi < 2; ++gi) {
-        const int rb = plan[wave][gi][0];
+        const int rb = plan_rb(gi);
         const int r = 16 * (rb < 0 ? 0 : rb) + m;
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
@@ -605,7 +613,7 @@ __global__ __launch_bounds__(kThreads, BF16 ? 3 : (DK == 128 ? 1 : 2)) void k1_p
     if constexpr (L2) {
 #pragma unroll
         for (int gi = 0; gi < 2; ++gi) {
-            const int rb = plan[wave][gi][0];
+            const int rb = plan_rb(gi);
             if (rb < 0) break;
             float ss = 0.f;
 #pragma unroll
@@ -747,7 +755,7 @@ __global__ __launch_bounds__(kThreads, BF16 ? 3 : (DK == 128 ? 1 : 2)) void k1_p
         }
 #pragma unroll
         for (int gi = 0; gi < 2; ++gi) {
-            const int rb = plan[wave][gi][0];
+            const int rb = plan_rb(gi);
             if (rb < 0) break;
             const int ref = 16 * rb;
             const int r = 16 * rb + m;
@@ -765,8 +773,8 @@ __global__ __launch_bounds__(kThreads, BF16 ? 3 : (DK == 128 ? 1 : 2)) void k1_p
             }
 #pragma unroll
             for (int k2 = 0; k2 < 2; ++k2) {
-                if (k2 >= plan[wave][gi][2]) break;
-                const int sb = plan[wave][gi][1] + k2;
+                if (k2 >= plan_cnt(gi)) break;
+                const int sb = plan_sb(gi) + k2;
                 const int s = 16 * sb + m;
                 if (sb == rb && ((slow_blocks >> rb) & 1u)) continue;  // after this loop
                 f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
@@ -788,12 +796,12 @@ __global__ __launch_bounds__(kThreads, BF16 ? 3 : (DK == 128 ? 1 : 2)) void k1_p
         // row-block operands and prefetched queries of the loop above are dead.
 #pragma unroll
         for (int gi = 0; gi < 2; ++gi) {
-            const int rb = plan[wave][gi][0];
+            const int rb = plan_rb(gi);
             if (rb < 0) break;
 #pragma unroll
             for (int k2 = 0; k2 < 2; ++k2) {
-                if (k2 >= plan[wave][gi][2]) break;
-                const int sb = plan[wave][gi][1] + k2;
+                if (k2 >= plan_cnt(gi)) break;
+                const int sb = plan_sb(gi) + k2;
                 if (sb != rb || !((slow_blocks >> rb) & 1u)) continue;
                 const int ref = 16 * rb;
                 const int r = 16 * rb + m;
@@ -901,12 +909,12 @@ __global__ __launch_bounds__(kThreads, BF16 ? 3 : (DK == 128 ? 1 : 2)) void k1_p
     // K is no longer read: the A tiles go to its LDS
 #pragma unroll
     for (int gi = 0; gi < 2; ++gi) {
-        const int rb = plan[wave][gi][0];
+        const int rb = plan_rb(gi);
         if (rb < 0) break;
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
-            if (k2 >= plan[wave][gi][2]) break;
-            const int sb = plan[wave][gi][1] + k2;
+            if (k2 >= plan_cnt(gi)) break;
+            const int sb = plan_sb(gi) + k2;
 #pragma unroll
             for (int i = 0; i < 4; ++i) sA[16 * rb + 4 * q + i][16 * sb + m] = aT[2 * gi + k2][i];
         }
@@ -976,14 +984,21 @@ __global__ __launch_bounds__(kThreads, BF16 ? 3 : (DK == 128 ? 1 : 2)) void k1_p
         if (wave == 0)  // (3,0)
             finish(mma_acc(mma_acc(mma_acc(z, 3, 0, 0), 3, 1, 0), 3, 2, 0), 3, 0);
         __syncthreads();
-        // move the parked blocks into the lower triangle and clear the upper one
-        const int blocks[6][2] = {{1, 0}, {2, 1}, {3, 2}, {2, 0}, {3, 1}, {3, 0}};
-        for (int idx = t; idx < 6 * 256; idx += kThreads) {
-            const int i = blocks[idx >> 8][0], j = blocks[idx >> 8][1];
-            const int r = (idx >> 4) & 15, c = idx & 15;
-            const float val = sA[16 * j + c][16 * i + r];
+        // move the parked blocks into the lower triangle and clear the upper
+        // one: thread t takes element (r, c) of every block. All six reads
+        // are issued before any write (one LDS round trip instead of six);
+        // no thread reads an element another thread writes.
+        static_assert(kThreads == 256, "one element per thread and block");
+        constexpr int blocks[6][2] = {{1, 0}, {2, 1}, {3, 2}, {2, 0}, {3, 1}, {3, 0}};
+        const int r = t >> 4, c = t & 15;
+        float val[6];
+#pragma unroll
+        for (int b = 0; b < 6; ++b) val[b] = sA[16 * blocks[b][1] + c][16 * blocks[b][0] + r];
+#pragma unroll
+        for (int b = 0; b < 6; ++b) {
+            const int i = blocks[b][0], j = blocks[b][1];
             sA[16 * j + c][16 * i + r] = 0.f;
-            sA[16 * i + r][16 * j + c] = val;
+            sA[16 * i + r][16 * j + c] = val[b];
         }
     }
     __syncthreads();
@@ -1022,9 +1037,9 @@ __global__ __launch_bounds__(kThreads, BF16 ? 3 : (DK == 128 ? 1 : 2)) void k1_p
     // Ab = Ainv diag(beta) A-frags: rows tokens (tile rt), K tokens (slab ts, permuted);
     // slabs (rt 0-1, ts 1) are identically zero (written in phase A).
     {
-        const int frags[6][2] = {{0, 0}, {1, 0}, {2, 0}, {2, 1}, {3, 0}, {3, 1}};
+        // frags (rt, ts): (0,0) (1,0) (2,0) (2,1) (3,0) (3,1)
         for (int f = wave; f < 6; f += 4) {
-            const int rt = frags[f][0], ts = frags[f][1];
+            const int rt = f < 2 ? f : (f >> 1) + 1, ts = f < 2 ? 0 : (f & 1);
             const int r = 16 * rt + m;
             Frag out;
 #pragma unroll
