@@ -2486,7 +2486,9 @@ hipError_t launch_typed(const PrefillArgs& a, hipStream_t stream) {
         switch (design) {
             case kTrio: launch_trio<DK, DV>(a, p, npairs, cus, lds_max, stream); break;
             case kQuad: launch_quad<DK, DV, 2>(a, p, npairs, stream); break;
-            case kNt4: launch_scan<DK, DV, 4, BF16>(a, p, npairs, stream); break;
+            case kNt4:  // bf16 only (fp32 inputs always take the 16-column kernel)
+                if constexpr (BF16) launch_scan<DK, DV, 4, BF16>(a, p, npairs, stream);
+                break;
             default: launch_scan<DK, DV, 1, BF16>(a, p, npairs, stream); break;
         }
         if (a.pos.num_pos > 0) {  // finish the states of positions inside a chunk
