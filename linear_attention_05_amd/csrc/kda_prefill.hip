@@ -581,6 +581,21 @@ __global__ __launch_bounds__(kThreads, BF16 ? 3 : (DK == 128 ? 1 : 2)) void k1_p
         }
     }
     constexpr int QDF = 4 * NKS / 4;  // Qd frags per wave
+    // q values of this wave's Qd handoff frags (phase A builds them first),
+    // loaded here with the rest so that their latency is hidden by the
+    // cumulative sum: frag f = wave + 4i, channels 32ks + 4q .. +3 and + 16
+    tin4 qd[QDF][2];
+#pragma unroll
+    for (int i = 0; i < QDF; ++i) {
+        const int f = wave + 4 * i;
+        const int rt = f / NKS, ks = f % NKS;
+        const int r = 16 * rt + m;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const tin4 qv = *reinterpret_cast<const tin4*>(row_ptr(Q, r) + 32 * ks + 16 * hh + 4 * q);
+            qd[i][hh] = qv;
+        }
+    }
 
 #pragma unroll
     for (int u = 0; u < KV; ++u) {
@@ -696,21 +711,6 @@ __global__ __launch_bounds__(kThreads, BF16 ? 3 : (DK == 128 ? 1 : 2)) void k1_p
     auto gdiff = [&](int a, int b, int c) -> float { return (float)(sG[a][c] - sG[b][c]); };
 
     f32x4 aT[4];  // A tiles of this wave's block pairs (slot 2*gi + k2)
-
-    // q values of this wave's Qd handoff frags (used at the end of phase A):
-    // frag f = wave + 4i, channels 32ks + 4q .. +3 and + 16
-    tin4 qd[QDF][2];
-#pragma unroll
-    for (int i = 0; i < QDF; ++i) {
-        const int f = wave + 4 * i;
-        const int rt = f / NKS, ks = f % NKS;
-        const int r = 16 * rt + m;
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-            const tin4 qv = *reinterpret_cast<const tin4*>(row_ptr(Q, r) + 32 * ks + 16 * hh + 4 * q);
-            qd[i][hh] = qv;
-        }
-    }
 
     // ---- phase A: 16x16 block pairs (rb, sb), sb <= rb, reference row 16*rb:
     // every factor e^(G_r - G_ref) (r >= ref) is <= 1 and e^(G_ref - G_s) is
