@@ -20,8 +20,10 @@
  *
  * Conventions shared by every entry point
  *   - Every tensor argument is a DEVICE pointer owned by the caller; the
- *     library never allocates, frees or retains memory. Scratch memory is
- *     passed in through `workspace` (size from kda_prefill_workspace_size).
+ *     library never allocates, frees or retains caller memory. Scratch memory
+ *     is passed in through `workspace` (size from kda_prefill_workspace_size),
+ *     except for kda_prefill_chunked_noalloc, which uses a fixed array the
+ *     library holds on each device instead.
  *   - All work is enqueued asynchronously on `stream` (0 = the null stream);
  *     no entry point synchronises. Results are visible after the caller
  *     synchronises the stream.
@@ -51,12 +53,16 @@
  *   - Decay range: the prefill keeps every decay factor it forms at or below
  *     1, so KDA's per-channel forgetting is handled down to alpha = 0 in any
  *     channel. It floors the per-token log-decay at -16 nats with bf16 q/k/v
- *     and at -64 nats with fp32 q/k/v (alpha >= 1.1e-7 resp. 1.6e-28); the
- *     results change by less than 1.2e-7 of the largest state entry. The
- *     decode step applies exp(g) as given.
- *   - The library keeps no global state besides the loaded code object and
- *     is reentrant; calls on different streams may run concurrently if they
- *     write disjoint outputs and workspaces.
+ *     and at -64 nats with fp32 q/k/v (alpha >= 1.1e-7 resp. 1.6e-28): each
+ *     state column moves by at most that fraction of its norm, and later
+ *     steps never enlarge the difference, so results change by about 1e-7 of
+ *     the state's magnitude. The decode step applies exp(g) as given.
+ *   - The library keeps no global state besides the loaded code object, the
+ *     device attributes it caches per device on first use, and the scratch
+ *     array of kda_prefill_chunked_noalloc. It is reentrant; calls on
+ *     different streams may run concurrently if they write disjoint outputs
+ *     and workspaces (calls of kda_prefill_chunked_noalloc on one device
+ *     share its array and must not overlap).
  */
 #ifndef KDA_H
 #define KDA_H
