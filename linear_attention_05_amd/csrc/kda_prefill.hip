@@ -489,7 +489,7 @@ __global__ __launch_bounds__(kThreads, BF16 ? 3 : (DK == 128 ? 1 : 2)) void k1_p
     // results need differences of G exact to about 1e-9)
     using GS = typename std::conditional<BF16, float, double>::type;
     __shared__ __attribute__((aligned(16))) GS sG[C][GP];  // g, then G * log2(e)
-    __shared__ float sB[C];
+    __shared__ __attribute__((aligned(16))) float sB[C];
     __shared__ double sTot[NQ][DK];  // cumulative-sum partial totals
     __shared__ unsigned sSlow;       // bit b: diagonal block b needs the four-level products
     __shared__ float sQn[L2 ? C : 1];  // inverse query-row norms
@@ -724,10 +724,13 @@ __global__ __launch_bounds__(kThreads, BF16 ? 3 : (DK == 128 ? 1 : 2)) void k1_p
         // r' = 16rb + m -> P A-frag [rt = rb][slab sb/2], slots 4*(sb%2) + i of
         // lane (m + 16q).
         auto store_pair = [&](int gi, int k2, int rb, int sb, const f32x4& accA, const f32x4& accP) {
+            // beta of rows 16 rb + 4q .. +3, read whole (a conditional read per
+            // element became a branch and an LDS round trip each)
+            const f32x4 bv = *reinterpret_cast<const f32x4*>(&sB[16 * rb + 4 * q]);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int rr = 16 * rb + 4 * q + i, ss = 16 * sb + m;
-                aT[2 * gi + k2][i] = ss < rr ? sB[rr] * accA[i] : 0.f;
+                aT[2 * gi + k2][i] = ss < rr ? bv[i] * accA[i] : 0.f;
             }
             typedef E e4 __attribute__((ext_vector_type(4)));
             e4 pv;
@@ -867,12 +870,8 @@ __global__ __launch_bounds__(kThreads, BF16 ? 3 : (DK == 128 ? 1 : 2)) void k1_p
             typedef E e4 __attribute__((ext_vector_type(4)));
             *reinterpret_cast<e4*>(hb + HO::kP + ((size_t)(rb * 2 + sb / 2) * 64 + lane) * 8 + 4 * (sb % 2)) = e4{};
         }
-        // whole zero slabs (row tiles 0-1, token slab 1) of P and Ab
-        if (wave < 2) {
-            const Frag zf = {};
-            store_frag<Frag, E>(hb + HO::kP, wave * 2 + 1, lane, zf);
-            store_frag<Frag, E>(hb + HO::kAb, wave * 2 + 1, lane, zf);
-        }
+        // The slabs (row tiles 0-1, token slab 1) of P and Ab lie wholly
+        // above the diagonal: they are zero, and neither stored nor read.
         // Kc^T A-frags: rows channels (tile ct), K tokens (slab ts, permuted)
         for (int f = wave; f < NRT * 2; f += 4) {
             const int ct = f / 2, ts = f % 2;
@@ -938,7 +937,11 @@ __global__ __launch_bounds__(kThreads, BF16 ? 3 : (DK == 128 ? 1 : 2)) void k1_p
             acc = pair_sum16(acc);
             acc = pair_sum32(acc);
             const float xr = (r == c ? 1.f : 0.f) - acc;
-            xs[r >> 2] = (p == (r & 3)) ? xr : xs[r >> 2];
+            // lane p keeps rows 4u + p: xs[r >> 2] is still 0 in every lane
+            // that does not keep row r, so a masked add stores it without a
+            // branch (a branch here split the substitution into one block per
+            // row, and no LDS read could be issued ahead of its row)
+            xs[r >> 2] += (p == (r & 3) ? 1.f : 0.f) * xr;
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u) sA[16 * b + 4 * u + p][16 * b + c] = xs[u];
@@ -1140,10 +1143,14 @@ __global__ __launch_bounds__(kThreads) void k2_scan_kernel(
     auto load_ops = [&](Ops& op, int n, int grp) {
         const E* hb = reinterpret_cast<const E*>(hbase + (size_t)n * HO::kBytes);
         if (grp == 0) {
-#pragma unroll
-            for (int ts = 0; ts < 2; ++ts) {
-                op.ab[ts] = load_frag<Frag, E>(hb + HO::kAb, rt * 2 + ts, lane);
-                op.p[ts] = load_frag<Frag, E>(hb + HO::kP, rt * 2 + ts, lane);
+            op.ab[0] = load_frag<Frag, E>(hb + HO::kAb, rt * 2, lane);
+            op.p[0] = load_frag<Frag, E>(hb + HO::kP, rt * 2, lane);
+            if (rt >= 2) {  // token slab 1 of row tiles 0-1 is zero (not stored)
+                op.ab[1] = load_frag<Frag, E>(hb + HO::kAb, rt * 2 + 1, lane);
+                op.p[1] = load_frag<Frag, E>(hb + HO::kP, rt * 2 + 1, lane);
+            } else {
+                op.ab[1] = Frag{};
+                op.p[1] = Frag{};
             }
         } else if (grp == 1) {
 #pragma unroll
@@ -2301,7 +2308,8 @@ __global__ __launch_bounds__(kThreads) void advance_chunk_kernel(
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
 #pragma unroll
-        for (int ts = 0; ts < 2; ++ts) abf[rt][ts] = load_frag<Frag, E>(hb + HO::kAb, rt * 2 + ts, lane);
+        for (int ts = 0; ts < 2; ++ts)  // token slab 1 of row tiles 0-1 is zero (not stored)
+            abf[rt][ts] = (ts == 0 || rt >= 2) ? load_frag<Frag, E>(hb + HO::kAb, rt * 2 + ts, lane) : Frag{};
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) wnf[rt][ks] = load_frag<Frag, E>(hb + HO::kW, rt * NKS + ks, lane);
     }
