@@ -492,9 +492,12 @@ __global__ __launch_bounds__(kThreads, BF16 ? 3 : (DK == 128 ? 1 : 2)) void k1_p
     __shared__ __attribute__((aligned(16))) float sB[C];
     __shared__ double sTot[NQ][DK];  // cumulative-sum partial totals
     __shared__ unsigned sSlow;       // bit b: diagonal block b needs the four-level products
-    __shared__ float sQn[L2 ? C : 1];  // inverse query-row norms
     TIn(*sK)[KP] = reinterpret_cast<TIn(*)[KP]>(sKA);
     float(*sA)[AP] = reinterpret_cast<float(*)[AP]>(sKA);
+    // inverse query-row norms (front-end) in the unused padding of G's rows:
+    // a separate array took K1 over the LDS of three workgroups per CU
+    static_assert(GP > DK, "G rows are padded");
+    auto qn = [&](int r) -> float& { return *reinterpret_cast<float*>(&sG[r][DK]); };
 
     // Chunk-major, last chunk first, heads fastest: neighbouring workgroups
     // read neighbouring rows of q, k and g, and the blocks the scan needs first
@@ -640,7 +643,7 @@ __global__ __launch_bounds__(kThreads, BF16 ? 3 : (DK == 128 ? 1 : 2)) void k1_p
                 }
             ss += __shfl_xor(ss, 16);
             ss += __shfl_xor(ss, 32);
-            if (q == 0) sQn[16 * rb + m] = 1.f / sqrtf(ss + kL2Eps);  // rows shared by two waves get equal values
+            if (q == 0) qn(16 * rb + m) = 1.f / sqrtf(ss + kL2Eps);  // rows shared by two waves get equal values
         }
     }
     __syncthreads();
@@ -752,7 +755,7 @@ __global__ __launch_bounds__(kThreads, BF16 ? 3 : (DK == 128 ? 1 : 2)) void k1_p
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int c = 32 * ks + perm32(q, e);
-                out[e] = (E)(qf(qd[i][e >> 2][e & 3]) * (L2 ? sQn[r] : 1.f) * fast_exp2((float)sG[r][c]));
+                out[e] = (E)(qf(qd[i][e >> 2][e & 3]) * (L2 ? qn(r) : 1.f) * fast_exp2((float)sG[r][c]));
             }
             store_frag<Frag, E>(hb + HO::kQd, rt * NKS + ks, lane, out);
         }
@@ -762,7 +765,7 @@ __global__ __launch_bounds__(kThreads, BF16 ? 3 : (DK == 128 ? 1 : 2)) void k1_p
             if (rb < 0) break;
             const int ref = 16 * rb;
             const int r = 16 * rb + m;
-            const float zq = L2 ? sQn[r] : 1.f;
+            const float zq = L2 ? qn(r) : 1.f;
             Frag X[NKS], Z[NKS];
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
@@ -808,7 +811,7 @@ __global__ __launch_bounds__(kThreads, BF16 ? 3 : (DK == 128 ? 1 : 2)) void k1_p
                 if (sb != rb || !((slow_blocks >> rb) & 1u)) continue;
                 const int ref = 16 * rb;
                 const int r = 16 * rb + m;
-                const float zq = L2 ? sQn[r] : 1.f;
+                const float zq = L2 ? qn(r) : 1.f;
                 f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
                 // Four levels h = 8, 4, 2, 1 over the local row index
                 // (lane row m): rows with bit h set (r side) take
