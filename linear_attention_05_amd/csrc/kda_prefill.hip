@@ -1737,9 +1737,10 @@ __global__ __launch_bounds__(192) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 }
 
 // Five-wave scan: one workgroup = one (sequence, head) and two column blocks
-// of 16 value columns, on one CU. A CU's vector-memory path delivers about
-// 50 B/clk from L2, and that bounds a scan step; so the operands both column
-// blocks need (W, Kc^T; Qd, P) are fetched once per CU.
+// of 16 value columns, on one CU. The rate at which a CU's vector-memory
+// path takes loads (about 25 B/clk when every CU streams) bounds a scan
+// step; so the operands both column blocks need (W, Kc^T; Qd, P) are
+// fetched once per CU.
 //   waves 0, 1  the chains of the two column blocks: U = U0 - W S, then
 //               S <- diag(Gamma_last) S + Kc^T U, with S in registers and W,
 //               Kc^T read from LDS one step ahead.
@@ -2472,12 +2473,14 @@ hipError_t launch_typed(const PrefillArgs& a, hipStream_t stream) {
                            a.num_seqs, a.total_tokens, a.H, p.max_chunks, a.frontend, p.handoff);
     }
     // Scan design. Every scan workgroup streams the whole handoff of its
-    // (sequence, head) through its CU, about 63 KB per chunk for D = 128, and
-    // a CU's vector-memory path (~50 B/clk from L2) bounds each chunk step.
-    // Measured chunk-step times on MI355X (D = 128): three-wave kernel, one
-    // 16-column block per CU: 1.35 us; five-wave kernel, two blocks sharing a
-    // CU's operand stream: 1.58 us; four-wave kernel with 64 columns: 3.08 us
-    // (with 16 or 32 columns, 1.73 and 2.11 us: never the best choice). Pick
+    // (sequence, head) through its CU, about 62 KB per chunk for D = 128, and
+    // the rate at which a CU's vector-memory path takes those loads (about
+    // 25 B/clk when every CU streams) bounds each chunk step. Chunk-step
+    // times on MI355X (D = 128) when this rule was set: three-wave kernel,
+    // one 16-column block per CU: 1.35 us (1.2 now); five-wave kernel, two
+    // blocks sharing a CU's operand stream: 1.58 us; four-wave kernel with 64
+    // columns: 3.08 us (with 16 or 32 columns, 1.73 and 2.11 us: never the
+    // best choice). Pick
     // the least (rounds of workgroups over the CUs) x (step time): few
     // (sequence, head) pairs take the three-wave kernel, a few times more the
     // five-wave one, thousands the 64-column one. fp32 operands take the
