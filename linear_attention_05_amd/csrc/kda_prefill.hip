@@ -838,7 +838,8 @@ __global__ __launch_bounds__(kThreads, BF16 ? 3 : (DK == 128 ? 1 : 2)) void k1_p
 #pragma unroll
                         for (int e = 0; e < 8; ++e) {
                             const int c = 32 * ks + 8 * q + e;
-                            const float f = fast_exp2(up ? gdiff(r, oth, c) : gdiff(oth, r, c));
+                            const float d = gdiff(r, oth, c);  // both sides read: no branch
+                            const float f = fast_exp2(up ? d : -d);
                             const float kv = kval(r, c) * f;
                             const float qv = qf(qs[ks][e]) * zq * f;
                             Xl[e] = (E)(up ? kv : 0.f);
@@ -847,6 +848,7 @@ __global__ __launch_bounds__(kThreads, BF16 ? 3 : (DK == 128 ? 1 : 2)) void k1_p
                         }
                         tA = M::run(Xl, Yl, tA);  // rows r, cols s
                         tP = M::run(Yl, Zl, tP);  // P^T: rows s, cols r
+                        __builtin_amdgcn_sched_barrier(0);  // one slab's operands live at a time
                     }
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
