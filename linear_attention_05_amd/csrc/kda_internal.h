@@ -43,6 +43,18 @@ struct PosArgs {
     int num_pos = 0;
 };
 
+// A second scan over the same chunks in the same launch as the first (the
+// chunk-parallel path's scan of zero values from the identity): its values are
+// one zero row read for every token and head (token and head strides 0); its
+// initial and final states and its outputs have the first scan's shapes
+// (Dk == Dv). Only the bf16 five-wave scan runs it.
+struct TwinScan {
+    const void* zero_v = nullptr;  // >= Dv zero values; null: no second scan
+    const float* initial_state = nullptr;
+    float* final_state = nullptr;
+    float* o = nullptr;
+};
+
 struct PrefillArgs {
     const void* q;
     const void* k;
@@ -65,6 +77,7 @@ struct PrefillArgs {
     unsigned phases;    // bit 0: prepare (prep + K1), bit 1: scan (K2)
     unsigned frontend;  // kFront* bits (0: inputs used as given)
     PosArgs pos;
+    TwinScan twin;      // scan phase only, no checkpoints or positions
 };
 
 // Bytes of workspace the plain prefill path needs (prep, K1, one scan).
@@ -82,6 +95,10 @@ constexpr int kSizingCUs = 256;
 int prefill_split_segments(int64_t total_tokens, int num_seqs, int H, int Dk, int Dv, int cus);
 size_t prefill_split_workspace_bytes(int64_t total_tokens, int num_seqs, int H, int Dk, int Dv,
                                      bool bf16);
+
+// Whether a scan with a twin (TwinScan) in one launch beats two scans run one
+// after the other, for npairs (sequence, head) pairs and Dv value columns.
+bool prefill_twin_scan_pays(int npairs, int Dk, int Dv, bool bf16, int cus);
 
 // Entry of every prefill call: the chunk-parallel path when it applies and the
 // workspace allows it, else the plain path.

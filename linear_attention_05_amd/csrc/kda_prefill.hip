@@ -1756,14 +1756,18 @@ __global__ __launch_bounds__(192) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 // every wave drains its prologue loads before its loop and issues each
 // loop's loads in a fixed order; the V and handoff pointers are not
 // __restrict__, which keeps prefetches from moving across the barriers.
-template <int DK, int DV, int NCB>
+// TWIN: the grid also runs a second scan over the same handoff (TwinScan:
+// zero values, its own initial states, final states and outputs), its
+// workgroups beside the first scan's on the same XCD, so both read each
+// handoff line from that XCD's L2.
+template <int DK, int DV, int NCB, bool TWIN>
 __global__ __launch_bounds__(64 * (NCB + 3)) __attribute__((amdgpu_waves_per_eu(1, 2))) void k2_quad_kernel(
     const void* vin, const int32_t* __restrict__ cu, const int32_t* __restrict__ order,
     const int32_t* __restrict__ chunk_start, const int32_t* __restrict__ ckpt_base, int npairs,
     int64_t N, int H, int64_t max_chunks, const unsigned char* handoff,
     const float* __restrict__ s0, float* __restrict__ sfinal, int64_t interval,
     float* __restrict__ ckpt, int64_t ckpt_rows, PosArgs pos, float* __restrict__ o,
-    float* __restrict__ sink) {
+    float* __restrict__ sink, TwinScan tw) {
     using M = Mma<true>;
     using E = _Float16;
     using Frag = half8;
@@ -1773,13 +1777,15 @@ __global__ __launch_bounds__(64 * (NCB + 3)) __attribute__((amdgpu_waves_per_eu(
     constexpr int NST = DK / 16;    // state row tiles
     constexpr int NRT = C / 16;     // token row tiles
     constexpr int NVB = DV / 16;    // column blocks per (seq, head)
-    constexpr int NWG = NVB / NCB;  // workgroups per (seq, head)
+    constexpr int NWG = NVB / NCB;  // workgroups per (seq, head) and scan
+    constexpr int NSUB = TWIN ? 2 * NWG : NWG;  // workgroups sharing a handoff block
     constexpr int LPR = 2 * NCB;    // prep: lanes per V row segment (16 bytes each)
     constexpr int RPI = 64 / LPR;   // prep: V rows per load instruction
     constexpr int NWF = NRT * NKS;  // W fragments per chunk
     constexpr int NKF = NST * 2;    // Kc^T fragments per chunk
-    constexpr int kLines = (int)(HO::kBytes / 128);     // 128-byte lines per handoff block
-    constexpr int kLinesWg = (kLines + NWG - 1) / NWG;  // lines each workgroup touches
+    constexpr int kLines = (int)(HO::kBytes / 128);       // 128-byte lines per handoff block
+    constexpr int kLinesWg = (kLines + NSUB - 1) / NSUB;  // lines each workgroup touches
+    static_assert(!TWIN || DK == DV, "the twin's states have the first scan's shape");
     constexpr int NTH = (kLinesWg + 63) / 64;           // handoff touches per lane
 
     __shared__ __attribute__((aligned(16))) E sWK[3][NWF + NKF][64][8];   // W then Kc^T fragments
@@ -1791,9 +1797,20 @@ __global__ __launch_bounds__(64 * (NCB + 3)) __attribute__((amdgpu_waves_per_eu(
 
     const int id = blockIdx.x;
     const int xcd = id & 7, slot = id >> 3;
-    const int pair = xcd + 8 * (slot / NWG);
-    const int j0 = (slot % NWG) * 16 * NCB;  // first of the workgroup's columns
+    const int pair = xcd + 8 * (slot / NSUB);
+    const int sub = slot % NSUB;              // share of the handoff touches
+    const bool twin = TWIN && sub >= NWG;     // a workgroup of the second scan
+    const int j0 = (sub % NWG) * 16 * NCB;    // first of the workgroup's columns
     if (pair >= npairs) return;
+    if (twin) {
+        vin = tw.zero_v;
+        s0 = tw.initial_state;
+        sfinal = tw.final_state;
+        o = tw.o;
+    }
+    // value rows: token stride H * DV, head stride DV (the twin's one zero row: 0)
+    const int64_t vts = twin ? 0 : (int64_t)H * DV;
+    const int64_t vhs = twin ? 0 : DV;
     const int rank = pair / H, h = pair % H;
     const int seq = order ? order[rank] : rank;
     int64_t tstart = 0, L = N;
@@ -1819,7 +1836,7 @@ __global__ __launch_bounds__(64 * (NCB + 3)) __attribute__((amdgpu_waves_per_eu(
     auto vrow = [&](int n) {
         const int64_t left = L - (int64_t)n * C;
         const int64_t tok = tstart + (int64_t)n * C + (lane < left ? lane : left - 1);
-        return V + (tok * H + h) * (int64_t)DV + j0;
+        return V + tok * vts + h * vhs + j0;
     };
 
     if (wave < NCB) {
@@ -1953,7 +1970,7 @@ __global__ __launch_bounds__(64 * (NCB + 3)) __attribute__((amdgpu_waves_per_eu(
         int tline[NTH];
 #pragma unroll
         for (int k = 0; k < NTH; ++k) {
-            const int t = (slot % NWG) * kLinesWg + (lane + 64 * k < kLinesWg ? lane + 64 * k : kLinesWg - 1);
+            const int t = sub * kLinesWg + (lane + 64 * k < kLinesWg ? lane + 64 * k : kLinesWg - 1);
             tline[k] = t < kLines ? t : kLines - 1;
         }
         auto dma_wk = [&](int n) {
@@ -2027,7 +2044,7 @@ __global__ __launch_bounds__(64 * (NCB + 3)) __attribute__((amdgpu_waves_per_eu(
             for (int i = 0; i < LPR; ++i) {
                 const int r = RPI * i + lane / LPR;
                 const int64_t tok = tstart + (int64_t)n * C + (r < left ? r : left - 1);
-                vr[i] = *reinterpret_cast<const us8*>(V + (tok * H + h) * (int64_t)DV + j0 + 8 * vpiece);
+                vr[i] = *reinterpret_cast<const us8*>(V + tok * vts + h * vhs + j0 + 8 * vpiece);
             }
             const E* hb = hptr(n);
 #pragma unroll
@@ -2446,17 +2463,31 @@ void launch_trio(const PrefillArgs& a, const Plan& p, int npairs, int cus, int l
 
 // Five-wave scan: one workgroup per (pair, 32 columns), one per CU (its LDS
 // use, about 150 KB, keeps a second one off the CU).
-template <int DK, int DV, int NCB>
+template <int DK, int DV, int NCB, bool TWIN>
 void launch_quad(const PrefillArgs& a, const Plan& p, int npairs, hipStream_t stream) {
-    constexpr int NWG = DV / (16 * NCB);
+    constexpr int NWG = DV / (16 * NCB) * (TWIN ? 2 : 1);
     const bool varlen = a.cu_seqlens != nullptr;
     const int64_t groups = (npairs + 7) / 8;
     const unsigned grid = (unsigned)(groups * 8 * NWG);
-    hipLaunchKernelGGL((k2_quad_kernel<DK, DV, NCB>), dim3(grid), dim3(64 * (NCB + 3)), 0, stream,
+    hipLaunchKernelGGL((k2_quad_kernel<DK, DV, NCB, TWIN>), dim3(grid), dim3(64 * (NCB + 3)), 0, stream,
                        a.v, a.cu_seqlens, varlen ? p.order : nullptr,
                        varlen ? p.chunk_start : nullptr, varlen ? p.ckpt_base : nullptr, npairs,
                        a.total_tokens, a.H, p.max_chunks, p.handoff, a.initial_state, a.final_state,
-                       a.ckpt_interval, a.ckpt_states, a.ckpt_rows, a.pos, a.o, p.sink);
+                       a.ckpt_interval, a.ckpt_states, a.ckpt_rows, a.pos, a.o, p.sink, a.twin);
+}
+
+// Chunk-step times on MI355X (D = 128, us x 100) the scan choice works with.
+constexpr int64_t kStepTrio = 135, kStepQuad = 158, kStepNt4 = 308;
+
+// The least (rounds of workgroups over the CUs) x (step time) over the bf16
+// scans for `blocks` 16-column blocks of one scan.
+int64_t bf16_scan_cost(int64_t blocks, int Dv, int cus, int* which) {
+    auto rounds = [&](int64_t wgs) { return (wgs + cus - 1) / cus; };
+    const int64_t trio = rounds(blocks) * kStepTrio, quad = rounds((blocks + 1) / 2) * kStepQuad;
+    const int64_t nt4 = Dv % 64 == 0 ? rounds((blocks + 3) / 4) * kStepNt4 : INT64_MAX;
+    const int w = trio <= quad && trio <= nt4 ? 0 : (quad <= nt4 ? 1 : 2);
+    if (which) *which = w;
+    return w == 0 ? trio : (w == 1 ? quad : nt4);
 }
 
 template <int DK, int DV, bool BF16>
@@ -2482,7 +2513,7 @@ hipError_t launch_typed(const PrefillArgs& a, hipStream_t stream) {
     // one 16-column block per CU: 1.35 us (1.2 now); five-wave kernel, two
     // blocks sharing a CU's operand stream: 1.58 us; four-wave kernel with 64
     // columns: 3.08 us (with 16 or 32 columns, 1.73 and 2.11 us: never the
-    // best choice). Pick
+    // best choice). Pick (bf16_scan_cost, kStep* above)
     // the least (rounds of workgroups over the CUs) x (step time): few
     // (sequence, head) pairs take the three-wave kernel, a few times more the
     // five-wave one, thousands the 64-column one. fp32 operands take the
@@ -2492,16 +2523,22 @@ hipError_t launch_typed(const PrefillArgs& a, hipStream_t stream) {
     const int cus = di.cus, lds_max = di.lds_per_block;
     enum { kTrio, kQuad, kNt4, kNt1 } design = kNt1;
     if (BF16) {
-        const int64_t blocks = (int64_t)npairs * (DV / 16);  // 16-column blocks
-        auto rounds = [&](int64_t wgs) { return (wgs + cus - 1) / cus; };
-        const int64_t trio = rounds(blocks) * 135, quad = rounds(blocks / 2) * 158;
-        const int64_t nt4 = DV % 64 == 0 ? rounds(blocks / 4) * 308 : INT64_MAX;
-        design = trio <= quad && trio <= nt4 ? kTrio : (quad <= nt4 ? kQuad : kNt4);
+        int w = 0;
+        bf16_scan_cost((int64_t)npairs * (DV / 16), DV, cus, &w);
+        design = w == 0 ? kTrio : (w == 1 ? kQuad : kNt4);
+    }
+    if (scan && a.twin.zero_v) {  // both scans in one five-wave launch
+        if constexpr (BF16 && DK == DV) {
+            if (a.ckpt_interval != 0 || a.pos.num_pos != 0) return hipErrorInvalidValue;
+            launch_quad<DK, DV, 2, true>(a, p, npairs, stream);
+            return hipGetLastError();
+        }
+        return hipErrorInvalidValue;
     }
     if (scan) {
         switch (design) {
             case kTrio: launch_trio<DK, DV>(a, p, npairs, cus, lds_max, stream); break;
-            case kQuad: launch_quad<DK, DV, 2>(a, p, npairs, stream); break;
+            case kQuad: launch_quad<DK, DV, 2, false>(a, p, npairs, stream); break;
             case kNt4:  // bf16 only (fp32 inputs always take the 16-column kernel)
                 if constexpr (BF16) launch_scan<DK, DV, 4, BF16>(a, p, npairs, stream);
                 break;
@@ -2521,6 +2558,14 @@ hipError_t launch_typed(const PrefillArgs& a, hipStream_t stream) {
 }
 
 }  // namespace
+
+bool prefill_twin_scan_pays(int npairs, int Dk, int Dv, bool bf16, int cus) {
+    if (!bf16 || Dk != Dv || npairs <= 0 || cus <= 0) return false;
+    const int64_t blocks = (int64_t)npairs * (Dv / 16);
+    // one launch: the five-wave scan over both scans' blocks (two per workgroup)
+    const int64_t both = ((blocks + cus - 1) / cus) * kStepQuad;
+    return both < 2 * bf16_scan_cost(blocks, Dv, cus, nullptr);
+}
 
 size_t prefill_workspace_bytes(int64_t total_tokens, int num_seqs, int H, int Dk, int Dv,
                                bool bf16) {

@@ -19,7 +19,12 @@
 //      is X_p = S_end(p-1) and S_end(p) = M_p X_p + F_p;
 //   4. correct: o_t += oI_t X_p for every token of segments 1 .. P-1.
 // Both scans run P * H * D / 16 column blocks at once over chains P times
-// shorter; they are the plain path's kernels. The combine runs on fp32
+// shorter; they are the plain path's kernels. With bf16 inputs and Dk == Dv
+// they run in one launch of the five-wave scan when that pays: each of its
+// workgroups shares one handoff stream among two column blocks (of one scan),
+// the workgroups of both scans for a (segment, head) sit on one XCD and share
+// its L2, and scan B reads one zero row for all its values instead of a zero
+// tensor. The combine runs on fp32
 // matrix cores and the correction at fp32 accuracy (three fp16 passes on
 // hi/lo operand pairs, fp32 accumulation).
 #include "kda_internal.h"
@@ -335,6 +340,15 @@ size_t prefill_split_workspace_bytes(int64_t total_tokens, int num_seqs, int H, 
     return split_layout(total_tokens, P, H, Dk, Dv, bf16).end;
 }
 
+hipError_t launch_fix_dims(const float* fin_a, const float* fin_b, float* xst, const PrefillArgs& a,
+                           const float* o_i, int64_t N, int P, int64_t seg_chunks, hipStream_t stream) {
+    if (a.Dk == 128 && a.Dv == 128) return launch_fix<128, 128>(fin_a, fin_b, xst, a.final_state, o_i, a.o, N, a.H, P, seg_chunks, stream);
+    if (a.Dk == 128 && a.Dv == 64) return launch_fix<128, 64>(fin_a, fin_b, xst, a.final_state, o_i, a.o, N, a.H, P, seg_chunks, stream);
+    if (a.Dk == 64 && a.Dv == 128) return launch_fix<64, 128>(fin_a, fin_b, xst, a.final_state, o_i, a.o, N, a.H, P, seg_chunks, stream);
+    if (a.Dk == 64 && a.Dv == 64) return launch_fix<64, 64>(fin_a, fin_b, xst, a.final_state, o_i, a.o, N, a.H, P, seg_chunks, stream);
+    return hipErrorInvalidValue;
+}
+
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
     const bool eligible = a.cu_seqlens == nullptr && a.num_seqs == 1 && a.phases == 3u &&
                           a.ckpt_interval == 0 && a.pos.num_pos == 0 && a.total_tokens > 0;
@@ -367,7 +381,11 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
     void* zero_v = ws + L.zero_v;
     float* o_i = reinterpret_cast<float*>(ws + L.o_i);
 
-    const int64_t zero_vec4 = N * a.H * a.Dk * (a.bf16 ? 2 : 4) / 16;
+    // Both scans in one launch when that pays (bf16, Dk == Dv): the second
+    // reads one zero row for every token; else a zero value tensor.
+    const DeviceInfo di = device_info();
+    const bool twin = prefill_twin_scan_pays(P * a.H, a.Dk, a.Dv, a.bf16, di.cus);
+    const int64_t zero_vec4 = twin ? a.Dk * 2 / 16 : N * a.H * a.Dk * (a.bf16 ? 2 : 4) / 16;
     {
         const int64_t work = (int64_t)P * a.H * a.Dk * (a.Dk > a.Dv ? a.Dk : a.Dv);
         const int64_t most = work > zero_vec4 ? work : zero_vec4;
@@ -385,7 +403,21 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
     A.initial_state = init_a;
     A.final_state = fin_a;
     A.workspace_bytes = L.plain;
-    hipError_t e = launch_prefill_plain(A, stream);
+    hipError_t e;
+    if (twin) {
+        A.phases = 1u;  // prep + K1
+        e = launch_prefill_plain(A, stream);
+        if (e != hipSuccess) return e;
+        A.phases = 2u;  // scans A and B in one launch
+        A.twin.zero_v = zero_v;
+        A.twin.initial_state = init_b;
+        A.twin.final_state = fin_b;
+        A.twin.o = o_i;
+        e = launch_prefill_plain(A, stream);
+        if (e != hipSuccess) return e;
+        return launch_fix_dims(fin_a, fin_b, xst, a, o_i, N, P, seg_chunks, stream);
+    }
+    e = launch_prefill_plain(A, stream);
     if (e != hipSuccess) return e;
     PrefillArgs Bs = A;  // scan B: zero values from the identity -> M_p, oI
     Bs.v = zero_v;
@@ -396,11 +428,7 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
     Bs.phases = 2u;
     e = launch_prefill_plain(Bs, stream);
     if (e != hipSuccess) return e;
-    if (a.Dk == 128 && a.Dv == 128) return launch_fix<128, 128>(fin_a, fin_b, xst, a.final_state, o_i, a.o, N, a.H, P, seg_chunks, stream);
-    if (a.Dk == 128 && a.Dv == 64) return launch_fix<128, 64>(fin_a, fin_b, xst, a.final_state, o_i, a.o, N, a.H, P, seg_chunks, stream);
-    if (a.Dk == 64 && a.Dv == 128) return launch_fix<64, 128>(fin_a, fin_b, xst, a.final_state, o_i, a.o, N, a.H, P, seg_chunks, stream);
-    if (a.Dk == 64 && a.Dv == 64) return launch_fix<64, 64>(fin_a, fin_b, xst, a.final_state, o_i, a.o, N, a.H, P, seg_chunks, stream);
-    return hipErrorInvalidValue;
+    return launch_fix_dims(fin_a, fin_b, xst, a, o_i, N, P, seg_chunks, stream);
 }
 
 }  // namespace kda
