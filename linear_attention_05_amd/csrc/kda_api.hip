@@ -140,13 +140,15 @@ size_t kda_prefill_workspace_size(int64_t total_tokens, int32_t num_seqs, int32_
 
 int32_t kda_prefill_scan_segments(int64_t total_tokens, int32_t num_seqs, int32_t H, int32_t Dk,
                                   int32_t Dv, int32_t chunk_size, kda_dtype_t in_dtype) {
-    if (check_prefill_sizes(total_tokens, num_seqs, H, Dk, Dv, chunk_size, enum_bits(in_dtype)) != KDA_OK)
+    const int dt = enum_bits(in_dtype);
+    if (check_prefill_sizes(total_tokens, num_seqs, H, Dk, Dv, chunk_size, dt) != KDA_OK)
         return 0;
     const kda::DeviceInfo di = kda::device_info();
     if (!di.valid) return 1;
     const int cus = di.cus;
-    const int want = kda::prefill_split_segments(total_tokens, num_seqs, H, Dk, Dv, cus);
-    const int sized = kda::prefill_split_segments(total_tokens, num_seqs, H, Dk, Dv, kda::kSizingCUs);
+    const bool bf16 = dt == KDA_BF16;
+    const int want = kda::prefill_split_segments(total_tokens, num_seqs, H, Dk, Dv, bf16, cus);
+    const int sized = kda::prefill_split_segments(total_tokens, num_seqs, H, Dk, Dv, bf16, kda::kSizingCUs);
     const int P = want < sized ? want : sized;
     return P < 2 ? 1 : P;
 }

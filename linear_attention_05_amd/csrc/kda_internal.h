@@ -92,7 +92,8 @@ hipError_t launch_prefill_plain(const PrefillArgs& a, hipStream_t stream);
 // used), and the workspace it needs when the workspace is sized for
 // kSizingCUs (0 = never used for these sizes).
 constexpr int kSizingCUs = 256;
-int prefill_split_segments(int64_t total_tokens, int num_seqs, int H, int Dk, int Dv, int cus);
+int prefill_split_segments(int64_t total_tokens, int num_seqs, int H, int Dk, int Dv, bool bf16,
+                           int cus);
 size_t prefill_split_workspace_bytes(int64_t total_tokens, int num_seqs, int H, int Dk, int Dv,
                                      bool bf16);
 

@@ -41,8 +41,11 @@ size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 constexpr int kMaxSegments = 16;
 // Each segment spans at least this many chunks.
 constexpr int64_t kMinSegmentChunks = 8;
-// Fewer segments than this leave too little gain to pay for the second scan.
+// Fewer segments than this leave too little gain to pay for the second scan;
+// with both scans in one launch (bf16, Dk == Dv) it costs less, and three pay
+// (measured at T = 65536, D = 128: 1.13-1.17x at P = 3, 0.89-1.01x at P = 2).
 constexpr int kMinSegments = 6;
+constexpr int kMinSegmentsTwin = 3;
 
 // Workspace of the split path, after the plain path's workspace for P
 // pseudo-sequences (offsets in bytes, all 256-byte aligned).
@@ -301,7 +304,7 @@ hipError_t launch_fix(const float* fin_a, const float* fin_b, float* xst, float*
         hipLaunchKernelGGL((split_combine_kernel<DK, NP>), grid, block, 0, stream, fin_a, fin_b, \
                            xst, final_state, H, DV);                                           \
         break;
-        KDA_COMBINE(6) KDA_COMBINE(7) KDA_COMBINE(8) KDA_COMBINE(9)
+        KDA_COMBINE(3) KDA_COMBINE(4) KDA_COMBINE(5) KDA_COMBINE(6) KDA_COMBINE(7) KDA_COMBINE(8) KDA_COMBINE(9)
         KDA_COMBINE(10)
         KDA_COMBINE(11) KDA_COMBINE(12) KDA_COMBINE(13) KDA_COMBINE(14) KDA_COMBINE(15)
         KDA_COMBINE(16)
@@ -318,7 +321,8 @@ hipError_t launch_fix(const float* fin_a, const float* fin_b, float* xst, float*
 
 }  // namespace
 
-int prefill_split_segments(int64_t total_tokens, int num_seqs, int H, int Dk, int Dv, int cus) {
+int prefill_split_segments(int64_t total_tokens, int num_seqs, int H, int Dk, int Dv, bool bf16,
+                           int cus) {
     if (num_seqs != 1 || total_tokens <= 0 || cus <= 0) return 1;
     const int64_t nchunks = (total_tokens + 63) / 64;
     const int64_t blocks = (int64_t)H * ((Dk > Dv ? Dk : Dv) / 16);  // wider scan's workgroups
@@ -326,16 +330,16 @@ int prefill_split_segments(int64_t total_tokens, int num_seqs, int H, int Dk, in
     P = P < nchunks / kMinSegmentChunks ? P : nchunks / kMinSegmentChunks;
     P = P < kMaxSegments ? P : kMaxSegments;
     // two scans of 1/P of the chain plus the combine and the correction: measured
-    // on MI355X (D = 128, T = 65536) 3.3x faster than the plain scan at P = 16,
-    // 1.7x at P = 8, 1.05x at P = 4
-    if (P < kMinSegments) return 1;
+    // on MI355X (D = 128, T = 65536) with two scan launches 3.3x faster than the
+    // plain scan at P = 16, 1.7x at P = 8, 1.05x at P = 4
+    if (P < (bf16 && Dk == Dv ? kMinSegmentsTwin : kMinSegments)) return 1;
     const int64_t seg = (nchunks + P - 1) / P;
     return (int)((nchunks + seg - 1) / seg);
 }
 
 size_t prefill_split_workspace_bytes(int64_t total_tokens, int num_seqs, int H, int Dk, int Dv,
                                      bool bf16) {
-    const int P = prefill_split_segments(total_tokens, num_seqs, H, Dk, Dv, kSizingCUs);
+    const int P = prefill_split_segments(total_tokens, num_seqs, H, Dk, Dv, bf16, kSizingCUs);
     if (P < 2) return 0;
     return split_layout(total_tokens, P, H, Dk, Dv, bf16).end;
 }
@@ -357,8 +361,8 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
         const DeviceInfo di = device_info();
         if (di.valid) {
             const int cus = di.cus;
-            const int want = prefill_split_segments(a.total_tokens, 1, a.H, a.Dk, a.Dv, cus);
-            const int sized = prefill_split_segments(a.total_tokens, 1, a.H, a.Dk, a.Dv, kSizingCUs);
+            const int want = prefill_split_segments(a.total_tokens, 1, a.H, a.Dk, a.Dv, a.bf16, cus);
+            const int sized = prefill_split_segments(a.total_tokens, 1, a.H, a.Dk, a.Dv, a.bf16, kSizingCUs);
             // the workspace was sized for `sized` segments: never use more
             P = want < sized ? want : sized;
             if (P >= 2 && split_layout(a.total_tokens, P, a.H, a.Dk, a.Dv, a.bf16).end > a.workspace_bytes)

@@ -23,6 +23,10 @@ CASES = [  # H, Dk, Dv, dtype, T, initial state
     (3, 64, 128, "bf16", 5000, False),
     (2, 64, 64, "f32", 4000, False),
     (2, 128, 128, "f32", 3300, True),
+    # both scans in one launch (bf16, Dk == Dv) from three segments on
+    (8, 128, 128, "bf16", 4096, True),
+    (10, 128, 128, "bf16", 2048, True),
+    (6, 64, 64, "bf16", 3000, False),
 ]
 
 
@@ -60,7 +64,8 @@ def test_split_matches_oracle(H, Dk, Dv, dtype, T, init):
     P = segments(x)
     print(f"split prefill H={H} Dk={Dk} Dv={Dv} {dtype} T={T} init={init}: {P} segments",
           flush=True)
-    assert P >= 6, "these sizes should take the chunk-parallel scan"
+    assert P >= (3 if dtype == "bf16" and Dk == Dv else 6), \
+        "these sizes should take the chunk-parallel scan"
     r = recurrence.prefill(x.q, x.k, x.v, x.g, x.beta, x.cu_seqlens,
                            initial_state=x.initial_state)
     o, fs = run(x)
@@ -83,7 +88,8 @@ def test_split_without_final_state():
 
 def test_segment_rule():
     """The headline shape (32 heads) fills the device with the plain scan;
-    short sequences and varlen batches never split."""
+    short sequences and varlen batches never split; bf16 with Dk == Dv (both
+    scans in one launch) splits from three segments, other inputs from six."""
     import torch
     import linear_attention_05_amd as K
     bf = torch.bfloat16
@@ -91,7 +97,11 @@ def test_segment_rule():
     assert K.kda_prefill_scan_segments(1024, 1, 1, 128, 128, bf) == 1
     assert K.kda_prefill_scan_segments(8192, 2, 1, 128, 128, bf) == 1
     assert K.kda_prefill_scan_segments(8192, 1, 4, 128, 128, bf) == 8
-    assert K.kda_prefill_scan_segments(65536, 1, 8, 128, 128, bf) == 1
+    assert K.kda_prefill_scan_segments(65536, 1, 8, 128, 128, bf) == 4
+    assert K.kda_prefill_scan_segments(65536, 1, 10, 128, 128, bf) == 3
+    assert K.kda_prefill_scan_segments(65536, 1, 16, 128, 128, bf) == 1
+    assert K.kda_prefill_scan_segments(65536, 1, 8, 128, 128, torch.float32) == 1
+    assert K.kda_prefill_scan_segments(65536, 1, 8, 128, 64, bf) == 1
     assert K.kda_prefill_scan_segments(65536, 1, 1, 128, 128, bf) == 16
     assert K.kda_prefill_scan_segments(8192, 1, 1, 128, 128, bf, chunk_size=32) == 0
 
