@@ -78,6 +78,9 @@ struct PrefillArgs {
     unsigned frontend;  // kFront* bits (0: inputs used as given)
     PosArgs pos;
     TwinScan twin;      // scan phase only, no checkpoints or positions
+    // varlen schedule tables (chunk_start, ckpt_base, order at the start of the
+    // workspace) already written by the caller: the prepare phase skips prep
+    bool schedule_ready = false;
 };
 
 // Bytes of workspace the plain prefill path needs (prep, K1, one scan).

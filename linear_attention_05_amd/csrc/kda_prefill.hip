@@ -2495,7 +2495,7 @@ hipError_t launch_typed(const PrefillArgs& a, hipStream_t stream) {
     const Plan p = make_plan(a);
     const bool varlen = a.cu_seqlens != nullptr;
     const bool prepare = (a.phases & 1u) != 0, scan = (a.phases & 2u) != 0;
-    if (prepare && varlen)
+    if (prepare && varlen && !a.schedule_ready)
         hipLaunchKernelGGL(prep_kernel, dim3(1), dim3(kPrepThreads), 0, stream, a.cu_seqlens, a.num_seqs,
                            a.total_tokens, a.ckpt_interval, p.chunk_start, p.ckpt_base, p.order);
     if (prepare && p.max_chunks > 0 && a.total_tokens > 0) {

@@ -71,9 +71,13 @@ SplitLayout split_layout(int64_t N, int P, int H, int Dk, int Dv, bool bf16) {
 }
 
 // ---------------------------------------------------------------- fill ----
-// Pseudo-sequence boundaries, scan A's initial states (segment 0: the
-// caller's, else zeros), scan B's identity initial states, zero values.
-__global__ __launch_bounds__(kT) void split_fill_kernel(int32_t* __restrict__ pcu, int P,
+// Pseudo-sequence boundaries and their schedule tables (what the varlen prep
+// would compute: every segment but the last has seg_chunks chunks, none has
+// checkpoints, and longest first is index order), scan A's initial states
+// (segment 0: the caller's, else zeros), scan B's identity initial states,
+// zero values.
+__global__ __launch_bounds__(kT) void split_fill_kernel(int32_t* __restrict__ pcu,
+                                                        int32_t* __restrict__ tables, int P,
                                                         int64_t seg_tokens, int64_t N,
                                                         const float* __restrict__ s0,
                                                         float* __restrict__ init_a,
@@ -85,6 +89,11 @@ __global__ __launch_bounds__(kT) void split_fill_kernel(int32_t* __restrict__ pc
     if (tid <= P) {
         const int64_t b = tid * seg_tokens;
         pcu[tid] = (int32_t)(b < N ? b : N);
+        // chunk_start [P + 1], ckpt_base [P + 1], order [P]
+        const int64_t nchunks = (N + 63) / 64, c = tid * (seg_tokens / 64);
+        tables[tid] = (int32_t)(c < nchunks ? c : nchunks);
+        tables[P + 1 + tid] = 0;
+        if (tid < P) tables[2 * (P + 1) + tid] = (int32_t)tid;
     }
     const int64_t one = (int64_t)H * Dk * Dv;  // states of one pseudo-sequence
     for (int64_t i = tid; i < (int64_t)P * one; i += stride)
@@ -395,8 +404,8 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
         const int64_t most = work > zero_vec4 ? work : zero_vec4;
         int64_t blocks = (most + kT - 1) / kT;
         blocks = blocks < 4096 ? blocks : 4096;
-        hipLaunchKernelGGL(split_fill_kernel, dim3((unsigned)blocks), dim3(kT), 0, stream, pcu, P,
-                           seg_chunks * 64, N, a.initial_state, init_a, init_b,
+        hipLaunchKernelGGL(split_fill_kernel, dim3((unsigned)blocks), dim3(kT), 0, stream, pcu,
+                           static_cast<int32_t*>(a.workspace), P, seg_chunks * 64, N, a.initial_state, init_a, init_b,
                            static_cast<f32x4*>(zero_v), zero_vec4, a.H, a.Dk, a.Dv);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -407,6 +416,7 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
     A.initial_state = init_a;
     A.final_state = fin_a;
     A.workspace_bytes = L.plain;
+    A.schedule_ready = true;  // written by the fill
     hipError_t e;
     if (twin) {
         A.phases = 1u;  // prep + K1
