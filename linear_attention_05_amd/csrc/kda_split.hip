@@ -197,11 +197,15 @@ __global__ __launch_bounds__(DK * 4) void split_combine_kernel(const float* __re
 // three passes of v_mfma_f32_16x16x32_f16 (hi hi, hi lo, lo hi) with fp32
 // accumulation: the dropped lo lo term is about 2^-22 of each product, so the
 // correction keeps fp32 accuracy at three times the fp16 rate instead of the
-// fp32 matrix-core rate (8x lower). One workgroup per (head, segment, pair of
+// fp32 matrix-core rate (8x lower). One workgroup per (head, segment, kGroup
 // chunks inside the segment); wave w owns value-column tiles w + 4 j, whose
-// X_p^T operand pairs stay in registers. The eight 16-token tiles are fully
-// unrolled and each tile's oI rows and old o values are loaded one tile ahead
-// (straight-line code: the waits cover only the tile in use).
+// X_p^T operand pairs stay in registers. Each 16-token tile of oI is loaded
+// once per workgroup (every thread a share, one tile ahead) into a
+// double-buffered LDS tile that all four waves read their operands from;
+// each wave loads the old o values of its own columns one tile ahead.
+// (Measured at T = 65536, H = 4, P = 8: 103 us with every wave loading the
+// whole oI tile itself, 83 us shared through LDS; 94 us with four chunks per
+// workgroup, 121 us loading two tiles ahead.)
 // Fragments: lane l holds row (A) or column (B) l % 16 at K = 8 (l / 16) + e.
 constexpr int kGroup = 2;  // chunks per workgroup
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
@@ -217,6 +221,10 @@ __global__ __launch_bounds__(kT) void split_correct_kernel(const float* __restri
     constexpr int CTW = DV / 64;  // column tiles per wave
     constexpr int KS = DK / 32;   // 32-wide K steps
     constexpr int NTILE = kGroup * 4;
+    constexpr int BP = DK + 4;           // padded LDS row of the oI tile
+    constexpr int NV = 16 * DK / 4 / kT;  // 16-byte oI pieces per thread and tile
+    static_assert(NV >= 1 && 16 * DK / 4 == NV * kT, "oI tile pieces spread evenly over the threads");
+    __shared__ __attribute__((aligned(16))) float sB[2][16][BP];
     const int h = (int)(blockIdx.x % (unsigned)H);
     const int64_t wg = (int64_t)(blockIdx.x / (unsigned)H);
     const int p = 1 + (int)(wg / groups_per_seg);
@@ -226,6 +234,9 @@ __global__ __launch_bounds__(kT) void split_correct_kernel(const float* __restri
     t_end = t_end < N ? t_end : N;
     const int64_t t_begin = c0 * 64;
     if (t_begin >= t_end) return;  // uniform over the workgroup
+    int64_t t_stop = t_begin + 64 * kGroup;
+    t_stop = t_stop < t_end ? t_stop : t_end;  // this workgroup's tokens: [t_begin, t_stop)
+    const int ntile = (int)((t_stop - t_begin + 15) / 16);
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int m = lane & 15, q = lane >> 4;
     // A = X_p^T: row 16 ct + m, K = 32 ks + 8 q + e
@@ -243,46 +254,56 @@ __global__ __launch_bounds__(kT) void split_correct_kernel(const float* __restri
                     alo[j][ks][e] = f16_lo(x);
                 }
     }
-    struct Tile {
-        f32x4 v[2 * KS];  // oI row pieces: K = 32 ks + 8 q + {0..3} and + {4..7}
-        f32x4 old[CTW];
-    };
-    // rows outside [t_begin, t_end) are read from t_begin (in bounds) and not stored
-    auto row_of = [&](int u) {
-        const int64_t tok = t_begin + 16 * u + m;
-        return (tok < t_end ? tok : t_begin) * H + h;
-    };
-    auto load_tile = [&](int u, Tile& tl) {
-        const int64_t row = row_of(u);
-        const float* src = o_i + row * (int64_t)DK + 8 * q;
+    // rows outside [t_begin, t_stop) are read from t_begin (in bounds) and not stored
+    auto row_at = [&](int64_t tok) { return (tok < t_stop ? tok : t_begin) * H + h; };
+    f32x4 stage[NV];  // this thread's share of the next oI tile
+    auto load_stage = [&](int u) {
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            tl.v[2 * ks] = *reinterpret_cast<const f32x4*>(src + 32 * ks);
-            tl.v[2 * ks + 1] = *reinterpret_cast<const f32x4*>(src + 32 * ks + 4);
+        for (int i = 0; i < NV; ++i) {
+            const int v = t + kT * i, r = v / (DK / 4), c = v % (DK / 4);
+            stage[i] = *reinterpret_cast<const f32x4*>(o_i + row_at(t_begin + 16 * u + r) * (int64_t)DK + 4 * c);
         }
-        const float* dst = o + row * (int64_t)DV + 4 * q;
-#pragma unroll
-        for (int j = 0; j < CTW; ++j) tl.old[j] = *reinterpret_cast<const f32x4*>(dst + 16 * (wave + 4 * j));
     };
-    Tile buf[2];
-    load_tile(0, buf[0]);
+    auto put_stage = [&](int b) {
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int v = t + kT * i, r = v / (DK / 4), c = v % (DK / 4);
+            *reinterpret_cast<f32x4*>(&sB[b][r][4 * c]) = stage[i];
+        }
+    };
+    f32x4 old[2][CTW];  // old o of this wave's columns, token m of the tile
+    auto load_old = [&](int u, f32x4* dst) {
+        const float* src = o + row_at(t_begin + 16 * u + m) * (int64_t)DV + 4 * q;
+#pragma unroll
+        for (int j = 0; j < CTW; ++j) dst[j] = *reinterpret_cast<const f32x4*>(src + 16 * (wave + 4 * j));
+    };
+    load_stage(0);
+    load_old(0, old[0]);
 #pragma unroll
     for (int u = 0; u < NTILE; ++u) {
-        if (u + 1 < NTILE) load_tile(u + 1, buf[(u + 1) & 1]);
-        const Tile& cur = buf[u & 1];
-        half8 bhi[KS], blo[KS];  // B = oI^T: column = token, K = 32 ks + 8 q + e
+        if (u >= ntile) break;  // uniform
+        put_stage(u & 1);
+        if (u + 1 < ntile) {
+            load_stage(u + 1);
+            load_old(u + 1, old[(u + 1) & 1]);
+        }
+        __syncthreads();  // tile u in LDS; every wave is done with tile u - 1
+        half8 bhi[KS], blo[KS];  // B = oI^T: column = token m, K = 32 ks + 8 q + e
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
+        for (int ks = 0; ks < KS; ++ks) {
+            const f32x4 v0 = *reinterpret_cast<const f32x4*>(&sB[u & 1][m][32 * ks + 8 * q]);
+            const f32x4 v1 = *reinterpret_cast<const f32x4*>(&sB[u & 1][m][32 * ks + 8 * q + 4]);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float x = e < 4 ? cur.v[2 * ks][e] : cur.v[2 * ks + 1][e - 4];
+                const float x = e < 4 ? v0[e] : v1[e - 4];
                 bhi[ks][e] = f16_hi(x);
                 blo[ks][e] = f16_lo(x);
             }
+        }
         f32x4 acc[CTW][2];
 #pragma unroll
         for (int j = 0; j < CTW; ++j) {
-            acc[j][0] = cur.old[j];
+            acc[j][0] = old[u & 1][j];
             acc[j][1] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
 #pragma unroll
@@ -294,7 +315,7 @@ __global__ __launch_bounds__(kT) void split_correct_kernel(const float* __restri
                 acc[j][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[j][ks], bhi[ks], acc[j][1], 0, 0, 0);
             }
         const int64_t tok = t_begin + 16 * u + m;
-        if (tok < t_end) {
+        if (tok < t_stop) {
             float* dst = o + (tok * H + h) * (int64_t)DV + 4 * q;
 #pragma unroll
             for (int j = 0; j < CTW; ++j) *reinterpret_cast<f32x4*>(dst + 16 * (wave + 4 * j)) = acc[j][0] + acc[j][1];
