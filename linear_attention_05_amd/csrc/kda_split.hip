@@ -26,7 +26,8 @@
 // its L2, and scan B reads one zero row for all its values instead of a zero
 // tensor. The combine runs on fp32
 // matrix cores and the correction at fp32 accuracy (three fp16 passes on
-// hi/lo operand pairs, fp32 accumulation).
+// hi/lo operand pairs scaled by powers of two, fp32 accumulation), for states
+// of any magnitude.
 #include "kda_internal.h"
 
 namespace kda {
@@ -189,15 +190,44 @@ __global__ __launch_bounds__(DK * 4) void split_combine_kernel(const float* __re
     }
 }
 
+// ------------------------------------------------ split fp16 products ----
+// The output correction runs its fp32 product on the fp16 matrix cores with
+// each operand split into a pair x = hi + lo of fp16 values and three passes of
+// v_mfma_f32_16x16x32_f16 (hi hi, hi lo, lo hi) accumulated in fp32: the
+// dropped lo lo term is about 2^-22 of each product, so the result keeps fp32
+// accuracy at three times the fp16 rate instead of the fp32 matrix-core rate
+// (8x lower). Each wave scales its operand by a power of two (exact) so that
+// its largest magnitude lies in [2^14, 2^15): every hi and lo then fits fp16,
+// whatever the magnitudes of the states, and the result is scaled back.
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+
+// Exponent k such that the wave's largest |x| (amax, this lane's share)
+// times 2^k lies in [2^14, 2^15); 0 when every value is zero.
+__device__ __forceinline__ int wave_scale_exp(float amax) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+    return amax > 0.f ? 15 - __builtin_amdgcn_frexp_expf(amax) : 0;
+}
+
+// x * 2^k split into fp16 hi and lo
+struct HalfPair {
+    _Float16 hi, lo;
+};
+__device__ __forceinline__ HalfPair split_pair(float x, int k) {
+    const float xs = ldexpf(x, k);
+    const _Float16 hi = (_Float16)xs;
+    return HalfPair{hi, (_Float16)(xs - (float)hi)};
+}
+
+__device__ __forceinline__ float abs_max4(float a, f32x4 v) {
+    return fmaxf(fmaxf(a, fmaxf(fabsf(v[0]), fabsf(v[1]))), fmaxf(fabsf(v[2]), fabsf(v[3])));
+}
+
 // ---------------------------------------------------------- correction ----
 // o_t += oI_t X_p for the tokens of segments 1 .. P-1, as the transposed
-// product (o_corr)^T = X_p^T oI^T, so that each lane's result is four
-// consecutive value columns of one token (16-byte read-modify-write of o).
-// Both operands are split into fp16 pairs x = hi + lo and the product takes
-// three passes of v_mfma_f32_16x16x32_f16 (hi hi, hi lo, lo hi) with fp32
-// accumulation: the dropped lo lo term is about 2^-22 of each product, so the
-// correction keeps fp32 accuracy at three times the fp16 rate instead of the
-// fp32 matrix-core rate (8x lower). One workgroup per (head, segment, kGroup
+// product (o_corr)^T = X_p^T oI^T (a split fp16 product, above), so that each
+// lane's result is four consecutive value columns of one token (16-byte
+// read-modify-write of o). One workgroup per (head, segment, kGroup
 // chunks inside the segment); wave w owns value-column tiles w + 4 j, whose
 // X_p^T operand pairs stay in registers. Each 16-token tile of oI is loaded
 // once per workgroup (every thread a share, one tile ahead) into a
@@ -208,10 +238,6 @@ __global__ __launch_bounds__(DK * 4) void split_combine_kernel(const float* __re
 // workgroup, 121 us loading two tiles ahead.)
 // Fragments: lane l holds row (A) or column (B) l % 16 at K = 8 (l / 16) + e.
 constexpr int kGroup = 2;  // chunks per workgroup
-typedef _Float16 half8 __attribute__((ext_vector_type(8)));
-
-__device__ __forceinline__ _Float16 f16_hi(float x) { return (_Float16)x; }
-__device__ __forceinline__ _Float16 f16_lo(float x) { return (_Float16)(x - (float)(_Float16)x); }
 
 template <int DK, int DV>
 __global__ __launch_bounds__(kT) void split_correct_kernel(const float* __restrict__ o_i,
@@ -239,19 +265,32 @@ __global__ __launch_bounds__(kT) void split_correct_kernel(const float* __restri
     const int ntile = (int)((t_stop - t_begin + 15) / 16);
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int m = lane & 15, q = lane >> 4;
-    // A = X_p^T: row 16 ct + m, K = 32 ks + 8 q + e
+    // A = X_p^T: row 16 ct + m, K = 32 ks + 8 q + e, scaled by 2^ka
     half8 ahi[CTW][KS], alo[CTW][KS];
+    int ka;
     {
         const float* X = xst + ((size_t)p * H + h) * DK * DV;
+        float xa[CTW][KS][8];
+        float am = 0.f;
 #pragma unroll
         for (int j = 0; j < CTW; ++j)
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const float x = X[(size_t)(32 * ks + 8 * q + e) * DV + 16 * (wave + 4 * j) + m];
-                    ahi[j][ks][e] = f16_hi(x);
-                    alo[j][ks][e] = f16_lo(x);
+                    xa[j][ks][e] = X[(size_t)(32 * ks + 8 * q + e) * DV + 16 * (wave + 4 * j) + m];
+                    am = fmaxf(am, fabsf(xa[j][ks][e]));
+                }
+        ka = wave_scale_exp(am);
+#pragma unroll
+        for (int j = 0; j < CTW; ++j)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const HalfPair hp = split_pair(xa[j][ks][e], ka);
+                    ahi[j][ks][e] = hp.hi;
+                    alo[j][ks][e] = hp.lo;
                 }
     }
     // rows outside [t_begin, t_stop) are read from t_begin (in bounds) and not stored
@@ -288,22 +327,27 @@ __global__ __launch_bounds__(kT) void split_correct_kernel(const float* __restri
             load_old(u + 1, old[(u + 1) & 1]);
         }
         __syncthreads();  // tile u in LDS; every wave is done with tile u - 1
-        half8 bhi[KS], blo[KS];  // B = oI^T: column = token m, K = 32 ks + 8 q + e
+        half8 bhi[KS], blo[KS];  // B = oI^T: column = token m, K = 32 ks + 8 q + e, scaled by 2^kb
+        f32x4 vb[2 * KS];
+        float bm = 0.f;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const f32x4 v0 = *reinterpret_cast<const f32x4*>(&sB[u & 1][m][32 * ks + 8 * q]);
-            const f32x4 v1 = *reinterpret_cast<const f32x4*>(&sB[u & 1][m][32 * ks + 8 * q + 4]);
+        for (int i = 0; i < 2 * KS; ++i) {
+            vb[i] = *reinterpret_cast<const f32x4*>(&sB[u & 1][m][32 * (i >> 1) + 8 * q + 4 * (i & 1)]);
+            bm = abs_max4(bm, vb[i]);
+        }
+        const int kb = wave_scale_exp(bm);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float x = e < 4 ? v0[e] : v1[e - 4];
-                bhi[ks][e] = f16_hi(x);
-                blo[ks][e] = f16_lo(x);
+                const HalfPair hp = split_pair(vb[2 * ks + (e >> 2)][e & 3], kb);
+                bhi[ks][e] = hp.hi;
+                blo[ks][e] = hp.lo;
             }
-        }
         f32x4 acc[CTW][2];
 #pragma unroll
         for (int j = 0; j < CTW; ++j) {
-            acc[j][0] = old[u & 1][j];
+            acc[j][0] = f32x4{0.f, 0.f, 0.f, 0.f};
             acc[j][1] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
 #pragma unroll
@@ -318,7 +362,13 @@ __global__ __launch_bounds__(kT) void split_correct_kernel(const float* __restri
         if (tok < t_stop) {
             float* dst = o + (tok * H + h) * (int64_t)DV + 4 * q;
 #pragma unroll
-            for (int j = 0; j < CTW; ++j) *reinterpret_cast<f32x4*>(dst + 16 * (wave + 4 * j)) = acc[j][0] + acc[j][1];
+            for (int j = 0; j < CTW; ++j) {
+                const f32x4 r = acc[j][0] + acc[j][1];
+                f32x4 out;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) out[i] = old[u & 1][j][i] + ldexpf(r[i], -(ka + kb));
+                *reinterpret_cast<f32x4*>(dst + 16 * (wave + 4 * j)) = out;
+            }
         }
     }
 }

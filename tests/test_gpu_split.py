@@ -125,6 +125,25 @@ def test_split_with_frontend():
     assert_parity(fs.cpu().numpy(), r["final"], "bf16", "split final state, front-end")
 
 
+def test_split_large_states_f32():
+    """fp32 inputs have no fp16 range limit: with v and S0 scaled by 2^18 the
+    states reach ~1e5-1e6, beyond fp16, and the combine and the correction
+    (split fp16 products) must still give 2^18 times the unscaled result
+    (the recurrence is linear in (v, S0); scaling by a power of two is exact)."""
+    c = 2.0 ** 18
+    x = make_prefill([4096], 2, 128, 128, "f32", 4711, init_state=True)
+    assert segments(x) >= 6
+    big = make_prefill([4096], 2, 128, 128, "f32", 4711, init_state=True)
+    big.v[...] = x.v * c
+    big.initial_state[...] = x.initial_state * c
+    r = recurrence.prefill(x.q, x.k, x.v, x.g, x.beta, x.cu_seqlens,
+                           initial_state=x.initial_state)
+    o, fs = run(big)
+    assert np.abs(fs).max() > 65504.0, "the states should exceed the fp16 range"
+    assert_parity(o / c, r["o"], "f32", "split o, states beyond fp16")
+    assert_parity(fs / c, r["final"], "f32", "split final state, states beyond fp16")
+
+
 @pytest.mark.parametrize("H,seed", [(4, 4242), (1, 4243)])
 def test_split_full_size_sampled(H, seed):
     """The few-head workloads bench.py times (B=1, T=65536, D=128, bf16, S0),
