@@ -148,8 +148,21 @@ __global__ __launch_bounds__(DK * 4) void split_combine_kernel(const float* __re
 #pragma unroll
         for (int i = 0; i < 4; ++i) st.F[i] = Fp[(size_t)i * Dv];
     };
-    // X_1 = S_end(0) = F_0
-    for (int i = t; i < DK * 16; i += NT) sXs[1][i % 16][i / 16] = fin_a[((size_t)h * DK + i / 16) * Dv + j0 + i % 16];
+    // X_1 = S_end(0) = F_0 (all loads issued before the first LDS write)
+    constexpr int PER = DK * 16 / NT;  // state elements per thread
+    {
+        float x1[PER];
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int i = t + NT * k;
+            x1[k] = fin_a[((size_t)h * DK + i / 16) * Dv + j0 + i % 16];
+        }
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int i = t + NT * k;
+            sXs[1][i % 16][i / 16] = x1[k];
+        }
+    }
     // Step p uses buffer p % NB; the loads for step p + NB - 1 go into the
     // buffer step p - 1 has finished with. The segment count is a template
     // parameter and the loop fully unrolled: every buffer index is a constant
@@ -186,7 +199,11 @@ __global__ __launch_bounds__(DK * 4) void split_combine_kernel(const float* __re
             if (final_state == nullptr) break;
             dst += (size_t)h * sv;
         }
-        for (int i = t; i < DK * 16; i += NT) dst[(size_t)(i / 16) * Dv + j0 + i % 16] = sXs[p][i % 16][i / 16];
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int i = t + NT * k;
+            dst[(size_t)(i / 16) * Dv + j0 + i % 16] = sXs[p][i % 16][i / 16];
+        }
     }
 }
 
