@@ -59,6 +59,7 @@
 #include "kda_internal.h"
 
 #include <type_traits>
+#include <utility>
 
 namespace kda {
 namespace {
@@ -161,6 +162,16 @@ struct Handoff {
 size_t handoff_bytes(int Dk, bool bf16) {
     if (Dk == 64) return bf16 ? Handoff<64, true>::kBytes : Handoff<64, false>::kBytes;
     return bf16 ? Handoff<128, true>::kBytes : Handoff<128, false>::kBytes;
+}
+
+// f(std::integral_constant<int, k>) for k = 0 .. N-1, each k a constant
+template <typename F, int... Ks>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Ks...>) {
+    (f(std::integral_constant<int, Ks>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 template <typename Frag, typename E>
@@ -1259,21 +1270,44 @@ __global__ __launch_bounds__(kThreads) void k2_scan_kernel(
         // fragment of X (K x N) is also the A-operand fragment of X^T, so O^T
         // takes the same fragments with the operands swapped; its result tile
         // gives each lane 4 adjacent value columns of one token (16-byte stores).
+        // The LDS fragments (V by slab, then S by K slab, column tile fastest)
+        // are read PD ahead of their products, so no product waits for a
+        // fresh LDS round trip.
         f32x4 U[NT], O[NT];
 #pragma unroll
         for (int ct = 0; ct < NT; ++ct) {
-            U[ct] = M::run(cur.ab[0], *reinterpret_cast<const Frag*>(&sV[0][ct][lane][0]), f32x4{0.f, 0.f, 0.f, 0.f});
-            U[ct] = M::run(cur.ab[1], *reinterpret_cast<const Frag*>(&sV[1][ct][lane][0]), U[ct]);
+            U[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
             O[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks)
-#pragma unroll
-            for (int ct = 0; ct < NT; ++ct) {
-                const Frag sf = *reinterpret_cast<const Frag*>(&sS[ks][ct][lane][0]);
-                U[ct] = M::run(cur.wn[ks], sf, U[ct]);
-                O[ct] = M::run(sf, cur.qd[ks], O[ct]);
-            }
+        {
+            constexpr int NR = (2 + NKS) * NT, PD = NT * 2 < NR ? NT * 2 : NR;
+            struct Rd {  // fragment k: V slab k / NT for k < 2 NT, else S slab k / NT - 2; column tile k % NT
+                static constexpr int slab(int k) { return k / NT; }
+            };
+            auto rd = [&](int k) -> Frag {
+                const int sl = k / NT, ct = k % NT;
+                return sl < 2 ? *reinterpret_cast<const Frag*>(&sV[sl][ct][lane][0])
+                              : *reinterpret_cast<const Frag*>(&sS[sl - 2][ct][lane][0]);
+            };
+            Frag pf[PD];
+            static_for<PD>([&](auto kc) {
+                constexpr int k = decltype(kc)::value;
+                pf[k] = rd(k);
+            });
+            static_for<NR>([&](auto kc) {
+                constexpr int k = decltype(kc)::value;
+                const Frag f = pf[k % PD];
+                if constexpr (k + PD < NR) pf[k % PD] = rd(k + PD);
+                constexpr int sl = Rd::slab(k), ct = k % NT;
+                if constexpr (sl < 2) {
+                    U[ct] = M::run(cur.ab[sl], f, U[ct]);
+                } else {
+                    U[ct] = M::run(cur.wn[sl - 2], f, U[ct]);
+                    O[ct] = M::run(f, cur.qd[sl - 2], O[ct]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            });
+        }
         // (d) publish U as B-frags (K = tokens): slab rt/2, half rt%2
 #pragma unroll
         for (int ct = 0; ct < NT; ++ct) {
@@ -1290,14 +1324,22 @@ __global__ __launch_bounds__(kThreads) void k2_scan_kernel(
         load_ops(nxt, pn, 3);
         __builtin_amdgcn_sched_barrier(0);
 
-        // (g) S <- diag(Gamma_last) S + Kc^T U  (on the dependency chain: first)
+        // (g) S <- diag(Gamma_last) S + Kc^T U  (on the dependency chain: first),
+        // every U fragment read before the first product
+        Frag uf[2][NT];
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct) {
+            uf[0][ct] = *reinterpret_cast<const Frag*>(&sU[0][ct][lane][0]);
+            uf[1][ct] = *reinterpret_cast<const Frag*>(&sU[1][ct][lane][0]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0; i < TPW; ++i)
 #pragma unroll
             for (int ct = 0; ct < NT; ++ct) {
                 f32x4 a = S[i][ct] * cur.gl[i];
-                a = M::run(cur.kc[i][0], *reinterpret_cast<const Frag*>(&sU[0][ct][lane][0]), a);
-                a = M::run(cur.kc[i][1], *reinterpret_cast<const Frag*>(&sU[1][ct][lane][0]), a);
+                a = M::run(cur.kc[i][0], uf[0][ct], a);
+                a = M::run(cur.kc[i][1], uf[1][ct], a);
                 S[i][ct] = a;
             }
 
@@ -1306,8 +1348,8 @@ __global__ __launch_bounds__(kThreads) void k2_scan_kernel(
         // end of the sequence stores to the sink)
 #pragma unroll
         for (int ct = 0; ct < NT; ++ct) {
-            O[ct] = M::run(*reinterpret_cast<const Frag*>(&sU[0][ct][lane][0]), cur.p[0], O[ct]);
-            O[ct] = M::run(*reinterpret_cast<const Frag*>(&sU[1][ct][lane][0]), cur.p[1], O[ct]);
+            O[ct] = M::run(uf[0][ct], cur.p[0], O[ct]);
+            O[ct] = M::run(uf[1][ct], cur.p[1], O[ct]);
         }
         {
             const int tok = 16 * rt + m;
