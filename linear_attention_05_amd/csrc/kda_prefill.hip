@@ -1280,10 +1280,8 @@ __global__ __launch_bounds__(kThreads) void k2_scan_kernel(
             O[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
         {
+            // fragment k: V slab k / NT for k < 2 NT, else S slab k / NT - 2; column tile k % NT
             constexpr int NR = (2 + NKS) * NT, PD = NT * 2 < NR ? NT * 2 : NR;
-            struct Rd {  // fragment k: V slab k / NT for k < 2 NT, else S slab k / NT - 2; column tile k % NT
-                static constexpr int slab(int k) { return k / NT; }
-            };
             auto rd = [&](int k) -> Frag {
                 const int sl = k / NT, ct = k % NT;
                 return sl < 2 ? *reinterpret_cast<const Frag*>(&sV[sl][ct][lane][0])
@@ -1298,7 +1296,7 @@ __global__ __launch_bounds__(kThreads) void k2_scan_kernel(
                 constexpr int k = decltype(kc)::value;
                 const Frag f = pf[k % PD];
                 if constexpr (k + PD < NR) pf[k % PD] = rd(k + PD);
-                constexpr int sl = Rd::slab(k), ct = k % NT;
+                constexpr int sl = k / NT, ct = k % NT;
                 if constexpr (sl < 2) {
                     U[ct] = M::run(cur.ab[sl], f, U[ct]);
                 } else {
