@@ -1151,7 +1151,6 @@ __global__ __launch_bounds__(kThreads) void k2_scan_kernel(
     float* my_sink = sink + ((size_t)(id & (kSinkSlots - 1)) * kThreads + t) * kSinkFloats;
     const unsigned char* hbase = handoff + ((size_t)h * max_chunks + cbase) * HO::kBytes;
 
-    // Issue every load of chunk n (0 <= n < nch: in bounds).
     // Issue the loads of chunk n (0 <= n < nch: in bounds) in four groups, so a
     // step can spread them over its phases instead of filling the memory
     // queue in one burst (a wave issues in order: a full queue would stall
