@@ -32,11 +32,15 @@
 // row must lie between s and r, which no single reference does for all
 // pairs; when the decay summed over the block is small in every channel
 // (below 2^12 for fp16 operands) the block still uses its first row (factors
-// in [2^-12, 2^12]: fp16 keeps full precision), otherwise the block is done
-// as four products, one per bit of the 16-row index: at level h the rows
-// with bit h set take e^(G_r - G_{start of r's h-run}) and the rows with bit
-// h clear take e^(G_{start of the next h-run} - G_s), and each product keeps
-// only the pairs whose highest differing index bit is h. The per-token
+// in [2^-12, 2^12]: fp16 keeps full precision). Otherwise the channels that
+// decay more than that over the block, when there are at most 32 of them,
+// are left out of its products and their pairs summed exactly in fp32 on the
+// vector units (each pair's factor 2^-|G_r - G_s| formed on its own); with
+// more, the block is done as four products, one per bit of the 16-row
+// index: at level h the rows with bit h set take e^(G_r - G_{start of r's
+// h-run}) and the rows with bit h clear take e^(G_{start of the next h-run}
+// - G_s), and each product keeps only the pairs whose highest differing
+// index bit is h. The per-token
 // log-decay is floored at -kGFloor nats (alpha >= e^-16 for bf16 inputs,
 // e^-64 for fp32: the change it makes to any result is below 1e-7 of the
 // state), which keeps |G| over a chunk small enough that differences of the
@@ -78,6 +82,10 @@ constexpr float kGFloorBF16 = 16.f, kGFloorF32 = 64.f;
 // a diagonal 16-row block keeps one reference row while the decay summed
 // over it stays below this many powers of two in every channel
 constexpr float kSpanLog2BF16 = 12.f, kSpanLog2F32 = 60.f;
+// a diagonal block with at most this many channels over the span sums those
+// channels' pairs on the vector units and the rest with one reference row;
+// with more it takes the four-level products
+constexpr int kSlowChannelsVALU = 32;
 
 
 __device__ __forceinline__ float bf16_to_f32(unsigned short b) {
@@ -502,7 +510,12 @@ __global__ __launch_bounds__(kThreads, BF16 ? 3 : (DK == 128 ? 1 : 2)) void k1_p
     __shared__ __attribute__((aligned(16))) GS sG[C][GP];  // g, then G * log2(e)
     __shared__ __attribute__((aligned(16))) float sB[C];
     __shared__ double sTot[NQ][DK];  // cumulative-sum partial totals
-    __shared__ unsigned sSlow;       // bit b: diagonal block b needs the four-level products
+    // bit c % 32 of word c / 32 of row b: channel c decays by more than
+    // 2^kSpanLog2 over diagonal block b
+    __shared__ unsigned sSlowCh[C / 16][NKS];
+    // per wave: its diagonal block's slow channels as a list (phase A)
+    static_assert(kSlowChannelsVALU % 4 == 0 && DK <= 256, "whole words of byte entries");
+    __shared__ unsigned char sSlowList[kThreads / 64][kSlowChannelsVALU];
     TIn(*sK)[KP] = reinterpret_cast<TIn(*)[KP]>(sKA);
     float(*sA)[AP] = reinterpret_cast<float(*)[AP]>(sKA);
     // inverse query-row norms (front-end) in the unused padding of G's rows:
@@ -573,21 +586,22 @@ __global__ __launch_bounds__(kThreads, BF16 ? 3 : (DK == 128 ? 1 : 2)) void k1_p
     //   qa[gi][ks]: row 16*rb + m, channels 32ks + 8q .. +7
     typedef TIn tin8 __attribute__((ext_vector_type(8)));
     typedef TIn tin4 __attribute__((ext_vector_type(4)));
-    // Block pairs of phase A: group gi of a wave takes row block rb (-1: no
-    // group) with column blocks sb .. sb + count - 1:
-    //   wave 0: rb 3 with sb 0-1, rb 0 with sb 0    wave 1: rb 3 with sb 2-3, rb 1 with sb 0
-    //   wave 2: rb 2 with sb 0-1                     wave 3: rb 2 with sb 2,   rb 1 with sb 1
-    // One nibble per wave in a constant (F: -1), read with the uniform wave
-    // index, so no table sits in memory.
-    auto nib = [&](unsigned k) { const int v = (int)((k >> (4 * wave)) & 15u); return v == 15 ? -1 : v; };
-    auto plan_rb = [&](int gi) { return nib(gi == 0 ? 0x2233u : 0x1F10u); };
-    auto plan_sb = [&](int gi) { return nib(gi == 0 ? 0x2020u : 0x1000u); };
-    auto plan_cnt = [&](int gi) { return nib(gi == 0 ? 0x1222u : 0x1011u); };
+    // Block pairs of phase A: group gi of a wave takes row block rb with
+    // column blocks sb .. sb + count - 1; group 1 is the wave's diagonal pair:
+    //   wave 0: rb 3 with sb 0-1, rb 0 with sb 0    wave 1: rb 3 with sb 2,   rb 3 with sb 3
+    //   wave 2: rb 2 with sb 0-1, rb 1 with sb 1    wave 3: rb 1 with sb 0,   rb 2 with sb 2
+    // (every wave two row-block operand sets and at most three pairs, and
+    // one diagonal block each, which may need the costlier forms below).
+    // One nibble per wave in a constant, read with the uniform wave index,
+    // so no table sits in memory.
+    auto nib = [&](unsigned k) { return (int)((k >> (4 * wave)) & 15u); };
+    auto plan_rb = [&](int gi) { return nib(gi == 0 ? 0x1233u : 0x2130u); };
+    auto plan_sb = [&](int gi) { return nib(gi == 0 ? 0x0020u : 0x2130u); };
+    auto plan_cnt = [&](int gi) { return nib(gi == 0 ? 0x1212u : 0x1111u); };
     tin8 qa[2][NKS];
 #pragma unroll
     for (int gi = 0; gi < 2; ++gi) {
-        const int rb = plan_rb(gi);
-        const int r = 16 * (rb < 0 ? 0 : rb) + m;
+        const int r = 16 * plan_rb(gi) + m;
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
             const tin8 qv = *reinterpret_cast<const tin8*>(row_ptr(Q, r) + 32 * ks + 8 * q);
@@ -635,7 +649,6 @@ __global__ __launch_bounds__(kThreads, BF16 ? 3 : (DK == 128 ? 1 : 2)) void k1_p
             for (int e = 0; e < 4; ++e) sG[r][c + e] = (double)gv[e];
         }
     }
-    if (t == 0) sSlow = 0u;
     if (t < C) sB[t] = ((front & kFrontBeta) && t < len) ? 1.f / (1.f + __expf(-breg)) : breg;
     // inverse query-row norms from this wave's phase-A rows: the four lanes
     // m + 16q hold the channels of row 16 rb + m between them
@@ -643,7 +656,6 @@ __global__ __launch_bounds__(kThreads, BF16 ? 3 : (DK == 128 ? 1 : 2)) void k1_p
 #pragma unroll
         for (int gi = 0; gi < 2; ++gi) {
             const int rb = plan_rb(gi);
-            if (rb < 0) break;
             float ss = 0.f;
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks)
@@ -698,6 +710,7 @@ __global__ __launch_bounds__(kThreads, BF16 ? 3 : (DK == 128 ? 1 : 2)) void k1_p
         double run = 0;
         for (int p = 0; p < grp; ++p) run += sTot[p][c];
         static_assert(RPQ % 16 == 0, "a row group holds whole 16-row blocks");
+    static_assert(DK % 64 == 0, "a wave's channels lie in one row group");
         GS first = 0;
 #pragma unroll
         for (int i = 0; i < RPQ; ++i) {
@@ -707,8 +720,17 @@ __global__ __launch_bounds__(kThreads, BF16 ? 3 : (DK == 128 ? 1 : 2)) void k1_p
             sG[r][c] = val;
             // decay over the 16-row block in this channel (G is non-increasing)
             if (i % 16 == 0) first = val;
-            if (i % 16 == 15 && first - val > (GS)(BF16 ? kSpanLog2BF16 : kSpanLog2F32))
-                atomicOr(&sSlow, 1u << (grp * (RPQ / 16) + i / 16));
+            if (i % 16 == 15) {
+                // a wave holds 64 consecutive channels of one row group: its
+                // vote is two whole words of the block's channel mask
+                const unsigned long long vote =
+                    __ballot(first - val > (GS)(BF16 ? kSpanLog2BF16 : kSpanLog2F32));
+                if (lane == 0) {
+                    const int b = grp * (RPQ / 16) + i / 16;
+                    sSlowCh[b][c / 32] = (unsigned)vote;
+                    sSlowCh[b][c / 32 + 1] = (unsigned)(vote >> 32);
+                }
+            }
         }
     }
     __syncthreads();
@@ -724,27 +746,39 @@ __global__ __launch_bounds__(kThreads, BF16 ? 3 : (DK == 128 ? 1 : 2)) void k1_p
     // (G_a - G_b) * log2(e) in channel c, differenced in the stored precision
     auto gdiff = [&](int a, int b, int c) -> float { return (float)(sG[a][c] - sG[b][c]); };
 
-    f32x4 aT[4];  // A tiles of this wave's block pairs (slot 2*gi + k2)
+    f32x4 aT[3];  // A tiles of this wave's block pairs: group 0 in slots 0-1, the diagonal in 2
 
     // ---- phase A: 16x16 block pairs (rb, sb), sb <= rb, reference row 16*rb:
     // every factor e^(G_r - G_ref) (r >= ref) is <= 1 and e^(G_ref - G_s) is
     // <= 1 for s < ref. Waves take the pairs grouped by rb so the row-block
-    // operands X = Kd', Z = Qd' are built once per rb. A diagonal pair whose
-    // block decays too much in some channel takes the four-level products.
-    const unsigned slow_blocks = __builtin_amdgcn_readfirstlane(sSlow);
+    // operands X = Kd', Z = Qd' are built once per rb. The wave's diagonal
+    // block (group 1) may hold slow channels: up to kSlowChannelsVALU of them
+    // are left out of its products and their pairs summed on the vector
+    // units; with more the pair takes the four-level products instead.
+    const int drb = plan_rb(1);
+    unsigned dmask[NKS];  // the diagonal block's slow channels (wave-uniform)
+    int nslow = 0;
+#pragma unroll
+    for (int w = 0; w < NKS; ++w) {
+        dmask[w] = __builtin_amdgcn_readfirstlane(sSlowCh[drb][w]);
+        nslow += __builtin_popcount(dmask[w]);
+    }
+    const bool dfour = nslow > kSlowChannelsVALU;
     {
         // A[r'][s'] with r' = 16rb + 4q + i, s' = 16sb + m, kept in registers
         // until every wave is done reading K; P^T[s'][r'] with s' = 16sb + 4q + i,
         // r' = 16rb + m -> P A-frag [rt = rb][slab sb/2], slots 4*(sb%2) + i of
-        // lane (m + 16q).
-        auto store_pair = [&](int gi, int k2, int rb, int sb, const f32x4& accA, const f32x4& accP) {
+        // lane (m + 16q). Stores P and returns the A tile (times beta, strictly
+        // lower part).
+        auto store_pair = [&](int rb, int sb, const f32x4& accA, const f32x4& accP) -> f32x4 {
             // beta of rows 16 rb + 4q .. +3, read whole (a conditional read per
             // element became a branch and an LDS round trip each)
             const f32x4 bv = *reinterpret_cast<const f32x4*>(&sB[16 * rb + 4 * q]);
+            f32x4 at;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int rr = 16 * rb + 4 * q + i, ss = 16 * sb + m;
-                aT[2 * gi + k2][i] = ss < rr ? bv[i] * accA[i] : 0.f;
+                at[i] = ss < rr ? bv[i] * accA[i] : 0.f;
             }
             typedef E e4 __attribute__((ext_vector_type(4)));
             e4 pv;
@@ -754,6 +788,7 @@ __global__ __launch_bounds__(kThreads, BF16 ? 3 : (DK == 128 ? 1 : 2)) void k1_p
                 pv[i] = (E)(ss <= rr ? accP[i] : 0.f);
             }
             *reinterpret_cast<e4*>(hb + HO::kP + ((size_t)(rb * 2 + sb / 2) * 64 + lane) * 8 + 4 * (sb % 2)) = pv;
+            return at;
         };
         // Qd A-frags (first, so that the prefetched queries die early): rows tokens (tile rt), K channels (slab ks, permuted)
 #pragma unroll
@@ -770,10 +805,9 @@ __global__ __launch_bounds__(kThreads, BF16 ? 3 : (DK == 128 ? 1 : 2)) void k1_p
             }
             store_frag<Frag, E>(hb + HO::kQd, rt * NKS + ks, lane, out);
         }
-#pragma unroll
-        for (int gi = 0; gi < 2; ++gi) {
-            const int rb = plan_rb(gi);
-            if (rb < 0) break;
+        // Group 0: off-diagonal pairs.
+        {
+            const int rb = plan_rb(0);
             const int ref = 16 * rb;
             const int r = 16 * rb + m;
             const float zq = L2 ? qn(r) : 1.f;
@@ -785,15 +819,14 @@ __global__ __launch_bounds__(kThreads, BF16 ? 3 : (DK == 128 ? 1 : 2)) void k1_p
                     const int c = 32 * ks + 8 * q + e;
                     const float fr = fast_exp2(gdiff(r, ref, c));
                     X[ks][e] = (E)(kval(r, c) * fr);
-                    Z[ks][e] = (E)(qf(qa[gi][ks][e]) * zq * fr);
+                    Z[ks][e] = (E)(qf(qa[0][ks][e]) * zq * fr);
                 }
             }
 #pragma unroll
             for (int k2 = 0; k2 < 2; ++k2) {
-                if (k2 >= plan_cnt(gi)) break;
-                const int sb = plan_sb(gi) + k2;
+                if (k2 >= plan_cnt(0)) break;
+                const int sb = plan_sb(0) + k2;
                 const int s = 16 * sb + m;
-                if (sb == rb && ((slow_blocks >> rb) & 1u)) continue;  // after this loop
                 f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int ks = 0; ks < NKS; ++ks) {
@@ -806,24 +839,112 @@ __global__ __launch_bounds__(kThreads, BF16 ? 3 : (DK == 128 ? 1 : 2)) void k1_p
                     accA = M::run(X[ks], Y, accA);  // rows r, cols s
                     accP = M::run(Y, Z[ks], accP);  // P^T: rows s, cols r
                 }
-                store_pair(gi, k2, rb, sb, accA, accP);
+                aT[k2] = store_pair(rb, sb, accA, accP);
             }
         }
-        // Diagonal pairs whose block decays too much: done here, where the
-        // row-block operands and prefetched queries of the loop above are dead.
+        // Group 1: the diagonal pair (r and s both run over rows 16 drb + m).
+        {
+            const int ref = 16 * drb;
+            const int r = ref + m;
+            const float zq = L2 ? qn(r) : 1.f;
+            f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
+            if (!dfour) {
+                // reference row 16 drb; slow channels are zero in the operand
+                // both products share (their factors may not fit it)
 #pragma unroll
-        for (int gi = 0; gi < 2; ++gi) {
-            const int rb = plan_rb(gi);
-            if (rb < 0) break;
+                for (int ks = 0; ks < NKS; ++ks) {
+                    const unsigned lb = dmask[ks] >> (8 * q);  // this lane's 8 channels
+                    Frag X, Y, Z;
 #pragma unroll
-            for (int k2 = 0; k2 < 2; ++k2) {
-                if (k2 >= plan_cnt(gi)) break;
-                const int sb = plan_sb(gi) + k2;
-                if (sb != rb || !((slow_blocks >> rb) & 1u)) continue;
-                const int ref = 16 * rb;
-                const int r = 16 * rb + m;
-                const float zq = L2 ? qn(r) : 1.f;
-                f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
+                    for (int e = 0; e < 8; ++e) {
+                        const int c = 32 * ks + 8 * q + e;
+                        const float d = gdiff(r, ref, c);
+                        const float kv = kval(r, c);
+                        const float fr = fast_exp2(d);
+                        X[e] = (E)(kv * fr);
+                        Z[e] = (E)(qf(qa[1][ks][e]) * zq * fr);
+                        Y[e] = ((lb >> e) & 1u) ? (E)0.f : (E)(kv * fast_exp2(-d));
+                    }
+                    accA = M::run(X, Y, accA);  // rows r, cols s
+                    accP = M::run(Y, Z, accP);  // P^T: rows s, cols r
+                }
+            }
+            if (nslow && !dfour) {
+                // The slow channels' pairs exactly, in fp32 on the vector
+                // units: A tile element i is the pair (r = 4q + i, s = m) when
+                // 4q + i > m, P^T tile element i the pair (s = 4q + i, r = m)
+                // otherwise; either way its factor is 2^-|G_4q+i - G_m| (G is
+                // non-increasing) times k_4q+i, and the other term k_m or q_m.
+                // The query of row m is held by lane m + 16 ((c % 32) / 8)
+                // (prefetched, element (c / 32, c % 8)): a uniformly indexed
+                // register read and a lane exchange. Four channels at a time;
+                // those past the last one get zero terms.
+                constexpr int QW = (int)sizeof(tin8) / 4;  // dwords per tin8
+                typedef unsigned qwords_t __attribute__((ext_vector_type(NKS * QW)));
+                typedef unsigned tin8w_t __attribute__((ext_vector_type(QW)));
+                qwords_t qw;
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) {
+                    const tin8w_t v = __builtin_bit_cast(tin8w_t, qa[1][ks]);
+#pragma unroll
+                    for (int j = 0; j < QW; ++j) qw[ks * QW + j] = v[j];
+                }
+                // the channel list: lane l places channel 64h + l at its rank
+                // among the block's slow channels
+                {
+                    int base = 0;
+#pragma unroll
+                    for (int hw = 0; hw < NKS / 2; ++hw) {
+                        const unsigned lo = dmask[2 * hw], hi = dmask[2 * hw + 1];
+                        const int rank = base + (int)__builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, 0u));
+                        const unsigned long long word = ((unsigned long long)hi << 32) | lo;
+                        if ((word >> lane) & 1ull) sSlowList[wave][rank] = (unsigned char)(64 * hw + lane);
+                        base += __builtin_popcountll(word);
+                    }
+                    // written and read by this wave only
+                    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                    __builtin_amdgcn_wave_barrier();
+                    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                }
+                bool up[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) up[i] = 4 * q + i > m;
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+                for (int j0 = 0; j0 < nslow; j0 += 4) {
+                    // four entries (bytes past the list's end are stale: masked
+                    // into range, their terms zero)
+                    const unsigned w4 = __builtin_amdgcn_readfirstlane(
+                        *reinterpret_cast<const unsigned*>(&sSlowList[wave][j0]));
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const bool ok = j0 + j < nslow;
+                        const int c = (int)((w4 >> (8 * j)) & (unsigned)(DK - 1));
+                        const int el = (c >> 5) * 8 + (c & 7);  // element of qa[1][.][.]
+                        const unsigned dw = qw[BF16 ? el >> 1 : el];
+                        const unsigned got = (unsigned)__shfl((int)dw, m + 16 * ((c & 31) >> 3));
+                        float qv;
+                        if constexpr (BF16) qv = bf16_to_f32((unsigned short)((c & 1) ? got >> 16 : got & 0xffffu));
+                        else qv = __uint_as_float(got);
+                        const float okf = ok ? 1.f : 0.f;  // a factor, not a branch around the loads
+                        const float km = kval(r, c) * okf;
+                        const float qm = qv * (zq * okf);
+                        const GS gm = sG[r][c];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int rr = ref + 4 * q + i;
+                            const float d = (float)(sG[rr][c] - gm);
+                            const float tk = kval(rr, c) * fast_exp2(-fabsf(d));
+                            acc[i] = fmaf(tk, up[i] ? km : qm, acc[i]);
+                        }
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    accA[i] += up[i] ? acc[i] : 0.f;
+                    accP[i] += up[i] ? 0.f : acc[i];
+                }
+            } else if (dfour) {
                 // Four levels h = 8, 4, 2, 1 over the local row index
                 // (lane row m): rows with bit h set (r side) take
                 // e^(G_m - G_{m & ~(h-1)}), rows with bit h clear (s side)
@@ -831,12 +952,6 @@ __global__ __launch_bounds__(kThreads, BF16 ? 3 : (DK == 128 ? 1 : 2)) void k1_p
                 // for r, s in one 2h-run on opposite sides of its middle
                 // their product is e^(G_r - G_s). Each level keeps only
                 // those pairs; P's diagonal (factor 1) is added at the end.
-                // The row's queries are read again (cache-hot) rather than
-                // kept live from the prefetch.
-                tin8 qs[NKS];
-#pragma unroll
-                for (int ks = 0; ks < NKS; ++ks)
-                    qs[ks] = *reinterpret_cast<const tin8*>(row_ptr(Q, r) + 32 * ks + 8 * q);
 #pragma unroll 1
                 for (int lv = 0; lv < 4; ++lv) {
                     const int hh = 8 >> lv;
@@ -852,7 +967,7 @@ __global__ __launch_bounds__(kThreads, BF16 ? 3 : (DK == 128 ? 1 : 2)) void k1_p
                             const float d = gdiff(r, oth, c);  // both sides read: no branch
                             const float f = fast_exp2(up ? d : -d);
                             const float kv = kval(r, c) * f;
-                            const float qv = qf(qs[ks][e]) * zq * f;
+                            const float qv = qf(qa[1][ks][e]) * zq * f;
                             Xl[e] = (E)(up ? kv : 0.f);
                             Zl[e] = (E)(up ? qv : 0.f);
                             Yl[e] = (E)(up ? 0.f : kv);
@@ -873,12 +988,12 @@ __global__ __launch_bounds__(kThreads, BF16 ? 3 : (DK == 128 ? 1 : 2)) void k1_p
 #pragma unroll
                 for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) dq += qf(qs[ks][e]) * kval(r, 32 * ks + 8 * q + e);
+                    for (int e = 0; e < 8; ++e) dq += qf(qa[1][ks][e]) * kval(r, 32 * ks + 8 * q + e);
                 dq = pair_sum32(pair_sum16(dq)) * zq;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) accP[i] += (4 * q + i == m) ? dq : 0.f;
-                store_pair(gi, k2, rb, sb, accA, accP);
             }
+            aT[2] = store_pair(drb, drb, accA, accP);
         }
         // zero halves inside stored slabs: (rb, sb) = (0, 1) and (2, 3)
         if (wave == 2 || wave == 3) {
@@ -923,17 +1038,13 @@ __global__ __launch_bounds__(kThreads, BF16 ? 3 : (DK == 128 ? 1 : 2)) void k1_p
 
     // K is no longer read: the A tiles go to its LDS
 #pragma unroll
-    for (int gi = 0; gi < 2; ++gi) {
-        const int rb = plan_rb(gi);
-        if (rb < 0) break;
+    for (int k2 = 0; k2 < 2; ++k2) {
+        if (k2 >= plan_cnt(0)) break;
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
-            if (k2 >= plan_cnt(gi)) break;
-            const int sb = plan_sb(gi) + k2;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sA[16 * rb + 4 * q + i][16 * sb + m] = aT[2 * gi + k2][i];
-        }
+        for (int i = 0; i < 4; ++i) sA[16 * plan_rb(0) + 4 * q + i][16 * (plan_sb(0) + k2) + m] = aT[k2][i];
     }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sA[16 * drb + 4 * q + i][16 * drb + m] = aT[2][i];
     __syncthreads();
 
     // ---- inverse: X = (I + A)^-1 in 16x16 blocks (all fp32).

@@ -19,7 +19,7 @@ from synth.inputs import PrefillInputs
 
 pytestmark = pytest.mark.gpu
 
-PATTERNS = ["mixed", "isolated", "stretch", "threshold"]
+PATTERNS = ["mixed", "isolated", "stretch", "threshold", "few"]
 
 
 def strong_g(x, pattern, seed):
@@ -30,7 +30,10 @@ def strong_g(x, pattern, seed):
     of 40 tokens get g = -1e4 and one token after them g = -inf. threshold:
     every channel a constant g per token, in [-0.55, -0.40] on even heads and
     [-0.70, -0.56] on odd heads: just below and just above the 16-token decay
-    (2^12) at which a diagonal block changes its product form."""
+    (2^12) at which a diagonal block changes its product form. few: on head h,
+    FEW[h % 6] channels draw g = -U(0.8, 20) per token (a block with at most
+    32 such channels sums their pairs apart from the others; 33 is the first
+    count past that)."""
     rng = np.random.default_rng(seed)
     g = x.g.copy()
     N, H, D = g.shape
@@ -53,9 +56,16 @@ def strong_g(x, pattern, seed):
         for h in range(H):  # even heads just below the change, odd heads just above
             lo, hi = (0.40, 0.55) if h % 2 == 0 else (0.56, 0.70)
             g[:, h, :] = -rng.uniform(lo, hi, size=(1, D)).astype(np.float32)
+    elif pattern == "few":
+        for h in range(H):
+            ch = rng.choice(D, size=FEW[h % len(FEW)], replace=False)
+            g[:, h, ch] = -rng.uniform(0.8, 20.0, size=(N, len(ch))).astype(np.float32)
     else:
         raise ValueError(pattern)
     return g
+
+
+FEW = [3, 33, 32, 1, 17, 8]
 
 
 def with_g(x, g):
@@ -131,7 +141,7 @@ def test_decay_range_positions(dtype, pattern):
 
 
 @pytest.mark.parametrize("H,Dk,Dv,dtype,T", [(1, 128, 128, "bf16", 4133), (2, 64, 64, "f32", 4000)])
-@pytest.mark.parametrize("pattern", ["mixed", "stretch"])
+@pytest.mark.parametrize("pattern", ["mixed", "stretch", "few"])
 def test_decay_range_chunk_parallel_scan(H, Dk, Dv, dtype, T, pattern):
     from test_gpu_split import run, segments
     x = make_prefill([T], H, Dk, Dv, dtype, 920 + H, init_state=True)
