@@ -459,9 +459,9 @@ __device__ __forceinline__ void locate_chunk(int ci, const int32_t* cu, const in
 // One workgroup per (chunk, head). Phases, separated by barriers:
 //   stage   K and g into LDS (16-byte loads), beta; g floored at -kGFloor;
 //           cumulative sum of g per channel in fp64, stored as G*log2(e) in
-//           place of g (fp32 for bf16 inputs, fp64 for fp32 inputs); which
-//           diagonal 16-row blocks decay by more than 2^kSpanLog2 in some
-//           channel (those take the four-level products)
+//           place of g (fp32 for bf16 inputs, fp64 for fp32 inputs); per
+//           diagonal 16-row block, the channels that decay by more than
+//           2^kSpanLog2 over it (slow channels, handled apart in phase A)
 //   A       the 10 lower 16x16 block pairs of A (to LDS) and of P (to the
 //           handoff); also the Qd, Kc^T and Gamma_last handoff
 //   inverse (I + A)^-1 by forward substitution, all four waves: wave w owns
@@ -515,7 +515,7 @@ __global__ __launch_bounds__(kThreads, BF16 ? 3 : (DK == 128 ? 1 : 2)) void k1_p
     __shared__ unsigned sSlowCh[C / 16][NKS];
     // per wave: its diagonal block's slow channels as a list (phase A)
     static_assert(kSlowChannelsVALU % 4 == 0 && DK <= 256, "whole words of byte entries");
-    __shared__ unsigned char sSlowList[kThreads / 64][kSlowChannelsVALU];
+    __shared__ __attribute__((aligned(4))) unsigned char sSlowList[kThreads / 64][kSlowChannelsVALU];
     TIn(*sK)[KP] = reinterpret_cast<TIn(*)[KP]>(sKA);
     float(*sA)[AP] = reinterpret_cast<float(*)[AP]>(sKA);
     // inverse query-row norms (front-end) in the unused padding of G's rows:

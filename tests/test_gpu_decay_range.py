@@ -125,7 +125,7 @@ def test_decay_range_every_scan(design, pattern):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("pattern", ["mixed", "stretch"])
+@pytest.mark.parametrize("pattern", ["mixed", "stretch", "few"])
 def test_decay_range_positions(dtype, pattern):
     from test_gpu_positions import gpu_at, oracle_states
     x = make_prefill([300, 129, 70], 2, 128, 128, dtype, 910, init_state=True)
