@@ -50,13 +50,17 @@
  *     so every element of v, of the states (the initial state and the state
  *     at each 64-token chunk boundary) and of the pseudo-values
  *     U = Ainv diag(beta) (V - K_decayed S) must have magnitude below 65504.
- *   - Decay range: the prefill keeps every decay factor it forms at or below
- *     1, so KDA's per-channel forgetting is handled down to alpha = 0 in any
- *     channel. It floors the per-token log-decay at -16 nats with bf16 q/k/v
- *     and at -64 nats with fp32 q/k/v (alpha >= 1.1e-7 resp. 1.6e-28): each
- *     state column moves by at most that fraction of its norm, and later
- *     steps never enlarge the difference, so results change by about 1e-7 of
- *     the state's magnitude. The decode step applies exp(g) as given.
+ *   - Decay range: every decay factor the prefill forms stays inside its
+ *     operand type's range: inside a 16-token block, channels that decay by
+ *     less than 2^12 (bf16 q/k/v; 2^60 with fp32) over the block share one
+ *     reference row there (factors up to that bound), and every other factor
+ *     is at most 1, so KDA's per-channel forgetting is handled down to
+ *     alpha = 0 in any channel. It floors the per-token log-decay at -16 nats
+ *     with bf16 q/k/v and at -64 nats with fp32 q/k/v (alpha >= 1.1e-7 resp.
+ *     1.6e-28): each state column moves by at most that fraction of its
+ *     norm, and later steps never enlarge the difference, so results change
+ *     by about 1e-7 of the state's magnitude. The decode step applies exp(g)
+ *     as given.
  *   - The library keeps no global state besides the loaded code object, the
  *     device attributes it caches per device on first use, and the scratch
  *     array of kda_prefill_chunked_noalloc. It is reentrant; calls on
