@@ -33,7 +33,7 @@
 // pairs; when the decay summed over the block is small in every channel
 // (below 2^12 for fp16 operands) the block still uses its first row (factors
 // in [2^-12, 2^12]: fp16 keeps full precision). Otherwise the channels that
-// decay more than that over the block, when there are at most 32 of them,
+// decay more than that over the block, when there are at most 16 of them,
 // are left out of its products and their pairs summed exactly in fp32 on the
 // vector units (each pair's factor 2^-|G_r - G_s| formed on its own); with
 // more, the block is done as four products, one per bit of the 16-row
@@ -85,7 +85,7 @@ constexpr float kSpanLog2BF16 = 12.f, kSpanLog2F32 = 60.f;
 // a diagonal block with at most this many channels over the span sums those
 // channels' pairs on the vector units and the rest with one reference row;
 // with more it takes the four-level products
-constexpr int kSlowChannelsVALU = 32;
+constexpr int kSlowChannelsVALU = 16;
 
 
 __device__ __forceinline__ float bf16_to_f32(unsigned short b) {
@@ -957,23 +957,26 @@ __global__ __launch_bounds__(kThreads, BF16 ? 3 : (DK == 128 ? 1 : 2)) void k1_p
                     const int hh = 8 >> lv;
                     const bool up = (m & hh) != 0;
                     const int oth = ref + (m & ~(hh - 1)) + (up ? 0 : hh);
+                    // factor 2^(G_ga - G_gb) <= 1: the rows are chosen per
+                    // lane once, so each element needs no select of its sign
+                    const int ga = up ? r : oth, gb = up ? oth : r;
                     f32x4 tA = {0.f, 0.f, 0.f, 0.f}, tP = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int ks = 0; ks < NKS; ++ks) {
-                        Frag Xl, Yl, Zl;
+                        Frag kf, qf8;
 #pragma unroll
                         for (int e = 0; e < 8; ++e) {
                             const int c = 32 * ks + 8 * q + e;
-                            const float d = gdiff(r, oth, c);  // both sides read: no branch
-                            const float f = fast_exp2(up ? d : -d);
-                            const float kv = kval(r, c) * f;
-                            const float qv = qf(qa[1][ks][e]) * zq * f;
-                            Xl[e] = (E)(up ? kv : 0.f);
-                            Zl[e] = (E)(up ? qv : 0.f);
-                            Yl[e] = (E)(up ? 0.f : kv);
+                            const float f = fast_exp2(gdiff(ga, gb, c));
+                            kf[e] = (E)(kval(r, c) * f);
+                            qf8[e] = (E)(qf(qa[1][ks][e]) * zq * f);
                         }
-                        tA = M::run(Xl, Yl, tA);  // rows r, cols s
-                        tP = M::run(Yl, Zl, tP);  // P^T: rows s, cols r
+                        // Every lane's row enters both sides unmasked: the
+                        // products of two r-side or two s-side rows (all
+                        // factors <= 1, so finite) are dropped below with
+                        // the pairs outside the level
+                        tA = M::run(kf, kf, tA);   // rows r, cols s
+                        tP = M::run(kf, qf8, tP);  // P^T: rows s, cols r
                         __builtin_amdgcn_sched_barrier(0);  // one slab's operands live at a time
                     }
 #pragma unroll

@@ -32,7 +32,7 @@ def strong_g(x, pattern, seed):
     [-0.70, -0.56] on odd heads: just below and just above the 16-token decay
     (2^12) at which a diagonal block changes its product form. few: on head h,
     FEW[h % 6] channels draw g = -U(0.8, 20) per token (a block with at most
-    32 such channels sums their pairs apart from the others; 33 is the first
+    16 such channels sums their pairs apart from the others; 17 is the first
     count past that)."""
     rng = np.random.default_rng(seed)
     g = x.g.copy()
@@ -65,7 +65,7 @@ def strong_g(x, pattern, seed):
     return g
 
 
-FEW = [3, 33, 32, 1, 17, 8]
+FEW = [3, 17, 16, 1, 33, 8]
 
 
 def with_g(x, g):
