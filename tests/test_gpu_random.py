@@ -77,3 +77,51 @@ def test_random_prefill_configuration(seed):
                                         initial_state=x.initial_state[s:s + 1] if init else None)
                 ref.append(rp["final"][0])
         assert_parity(ps.cpu().numpy(), np.stack(ref), dtype, "positions")
+
+
+def _strong_g(x, seed):
+    """A copy of x.g in which each head has a random number of channels (0 to
+    all of them, a few small counts likelier) drawing g = -U(0.5, 20) per
+    token: diagonal 16-token blocks then take every product form K1 has
+    (shared reference row, slow channels apart, four levels)."""
+    rng = np.random.default_rng([901, seed])
+    g = x.g.copy()
+    N, H, D = g.shape
+    for h in range(H):
+        n = int(rng.choice([0, 1, 2, 5, 16, 17, int(rng.integers(0, D + 1)), D]))
+        ch = rng.choice(D, size=n, replace=False)
+        g[:, h, ch] = -rng.uniform(0.5, 20.0, size=(N, n)).astype(np.float32)
+    return g
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_prefill_strong_decay(seed):
+    """The random configurations above (without the gate transform, whose raw
+    input replaces g) with fast-decaying channels per head."""
+    import torch
+    import linear_attention_05_amd as K
+    lengths, H, Dk, Dv, dtype, init, ckpt, front, _ = _config(seed)
+    front &= ~fe.FRONT_GATE
+    kw = dict(init_state=init, ckpt_interval=ckpt)
+    plain = make_prefill(lengths, H, Dk, Dv, dtype, 3000 + seed, **kw)
+    raw = make_prefill(lengths, H, Dk, Dv, dtype, 3000 + seed, raw=True, **kw)
+    pick = lambda bit, name: getattr(raw if front & bit else plain, name)
+    x = PrefillInputs(dtype, H, Dk, Dv, lengths, pick(fe.FRONT_L2NORM_QK, "q"),
+                      pick(fe.FRONT_L2NORM_QK, "k"), plain.v, _strong_g(plain, seed),
+                      pick(fe.FRONT_BETA_SIGMOID, "beta"), plain.initial_state,
+                      ckpt_interval=ckpt)
+    print(f"random strong-decay prefill seed {seed}: lengths={lengths} H={H} Dk={Dk} Dv={Dv} "
+          f"{dtype} init={init} ckpt={ckpt} front={front}", flush=True)
+    s0 = dev_tensor(x.initial_state) if init else None
+    o, fs, ck = K.kda_prefill_chunked(
+        dev_tensor(x.q), dev_tensor(x.k), dev_tensor(x.v), dev_tensor(x.g), dev_tensor(x.beta),
+        cu_seqlens=dev_tensor(x.cu_seqlens), initial_state=s0, ckpt_interval=ckpt,
+        num_checkpoints=x.num_checkpoints(), frontend=front)
+    torch.cuda.synchronize()
+    q, k, v, g, beta = fe.apply(x.q, x.k, x.v, x.g, x.beta, front)
+    r = recurrence.prefill(q, k, v, g, beta, x.cu_seqlens, initial_state=x.initial_state,
+                           ckpt_interval=ckpt)
+    assert_parity(o.cpu().numpy(), r["o"], dtype, "o")
+    assert_parity(fs.cpu().numpy(), r["final"], dtype, "final")
+    if ckpt and r["ckpt"].size:
+        assert_parity(ck.cpu().numpy(), r["ckpt"], dtype, "checkpoints")
