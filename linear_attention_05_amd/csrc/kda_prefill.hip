@@ -848,9 +848,10 @@ __global__ __launch_bounds__(kThreads, BF16 ? 3 : (DK == 128 ? 1 : 2)) void k1_p
             const int r = ref + m;
             const float zq = L2 ? qn(r) : 1.f;
             f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
-            if (!dfour) {
-                // reference row 16 drb; slow channels are zero in the operand
-                // both products share (their factors may not fit it)
+            // reference row 16 drb; slow channels are zero in the operand both
+            // products share (their factors may not fit it), a select only
+            // compiled into the copy for blocks that have them
+            auto diag_products = [&](auto masked) {
 #pragma unroll
                 for (int ks = 0; ks < NKS; ++ks) {
                     const unsigned lb = dmask[ks] >> (8 * q);  // this lane's 8 channels
@@ -863,12 +864,16 @@ __global__ __launch_bounds__(kThreads, BF16 ? 3 : (DK == 128 ? 1 : 2)) void k1_p
                         const float fr = fast_exp2(d);
                         X[e] = (E)(kv * fr);
                         Z[e] = (E)(qf(qa[1][ks][e]) * zq * fr);
-                        Y[e] = ((lb >> e) & 1u) ? (E)0.f : (E)(kv * fast_exp2(-d));
+                        const E y = (E)(kv * fast_exp2(-d));
+                        if constexpr (decltype(masked)::value) Y[e] = ((lb >> e) & 1u) ? (E)0.f : y;
+                        else Y[e] = y;
                     }
                     accA = M::run(X, Y, accA);  // rows r, cols s
                     accP = M::run(Y, Z, accP);  // P^T: rows s, cols r
                 }
-            }
+            };
+            if (nslow == 0) diag_products(std::false_type{});
+            else if (!dfour) diag_products(std::true_type{});
             if (nslow && !dfour) {
                 // The slow channels' pairs exactly, in fp32 on the vector
                 // units: A tile element i is the pair (r = 4q + i, s = m) when
