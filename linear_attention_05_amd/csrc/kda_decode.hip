@@ -9,7 +9,9 @@
 // fp32 state traffic per head and token (Kimi K3 report, "Key data"): under
 // one FLOP per byte, so the kernel is built for HBM bandwidth, with no MFMA.
 //
-// Mapping: one 512-thread workgroup per (b, h). Thread t owns the 4 adjacent
+// Mapping: one 512-thread workgroup per (b, h) (for batches that do not give
+// every CU 8 of them, 2 or 4 workgroups per (b, h), each owning a slice of
+// the value columns: decode_slices_kernel). Thread t owns the 4 adjacent
 // value columns 4*(t % CG) .. +3 (CG = Dv/4) of the key rows
 // rg, rg + RG, rg + 2*RG, ... (rg = t / CG, RG = 512/CG): one wave reads
 // 64/CG whole adjacent rows per 16-byte-per-lane load, so each load
@@ -145,12 +147,16 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
     if (front & kFrontBeta) bt = 1.f / (1.f + __expf(-bt));
     float kn = 1.f, qn = 1.f;  // inverse norms of k and q (L2)
     if constexpr (L2) {
+        // No contraction here: a lane's last square fused into the first
+        // exchange's addition would be unrounded in that lane only, and the
+        // lanes (so the row groups) would get different norms.
+#pragma clang fp contract(off)
         float sk = 0.f, sq = 0.f;
 #pragma unroll
         for (int j = 0; j < DK / 64; ++j) {
             const float kx = in_f32<BF16>(kw[j]), qx = in_f32<BF16>(qw[j]);
-            sk += kx * kx;
-            sq += qx * qx;
+            sk = j == 0 ? kx * kx : fmaf(kx, kx, sk);
+            sq = j == 0 ? qx * qx : fmaf(qx, qx, sq);
         }
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) {
@@ -217,15 +223,179 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
     }
 }
 
+// Column slices (few (b, h) pairs): the step of decode_kernel with NS
+// workgroups of 512 / NS threads per (b, h), slice j owning value columns
+// j DV/NS .. (j+1) DV/NS - 1 (every step of the update is per value column,
+// except k . q, which each slice forms itself). A thread keeps the tiling of
+// decode_kernel (rows rg, rg + RG, ... for RG = 2048 / DV row groups; 4
+// adjacent columns), and the reductions over row groups run in the same
+// order: a butterfly over each run of RGW = 256 / DV consecutive row groups
+// (one wave's worth in decode_kernel), then the RG / RGW run sums in
+// ascending order. So a (b, h) gets the same bits whatever its batch's size.
+template <int DK, int DV, int NS, bool BF16, bool L2>
+__global__ __launch_bounds__(kThreads / NS) void decode_slices_kernel(
+    const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
+    const float* __restrict__ g, const float* __restrict__ beta, float* __restrict__ state,
+    float* __restrict__ o, unsigned front) {
+    constexpr int NT = kThreads / NS;    // threads of this workgroup
+    constexpr int CG = DV / 4;           // column groups of the whole state
+    constexpr int CGS = CG / NS;         // column groups of this slice
+    constexpr int RG = kThreads / CG;    // row groups
+    constexpr int RPT = DK / RG;         // rows per thread
+    constexpr int RGW = 64 / CG;         // row groups per run (a wave at NS = 1)
+    constexpr int NRUN = RG / RGW;       // runs
+    static_assert(RPT * RG == DK && CG * 4 == DV && RGW >= 1 && CGS * NS == CG && CGS >= 1 &&
+                      NT % 64 == 0 && NRUN == kWaves,
+                  "bad decode tiling");
+
+    // per-row vectors: every thread stores its slots (rows past DK are never
+    // read), so no branch invites the compiler to sink the row loads behind
+    // the state loads
+    constexpr int RPS = (DK + NT - 1) / NT;  // per-row slots per thread
+    __shared__ float s_a[RPS * NT], s_k[RPS * NT], s_q[RPS * NT];
+    __shared__ f32x4 s_red[NRUN][CGS][2];
+    __shared__ float s_kq[NRUN];
+
+    const int t = threadIdx.x;
+    const int cgl = t % CGS;  // column group within the slice
+    const int rg = t / CGS;
+    const int lane = t & 63;
+    const int64_t pair = blockIdx.x / NS;  // b * H + h
+    const int cg = (int)(blockIdx.x % NS) * CGS + cgl;
+    float* S = state + pair * (int64_t)(DK * DV);
+
+    // 1. the small per-(b, h) inputs first: the memory counter completes in
+    // issue order, so waiting for them does not wait for the state
+    float graw[RPS];
+    raw_t<BF16> kraw[RPS], qraw[RPS];
+#pragma unroll
+    for (int j = 0; j < RPS; ++j) {
+        const int i = t + NT * j;
+        const int tr = i < DK ? i : DK - 1;  // unconditional loads (no branch to join)
+        graw[j] = g[pair * DK + tr];
+        kraw[j] = load_raw<BF16>(k, pair * DK + tr);
+        qraw[j] = load_raw<BF16>(q, pair * DK + tr);
+    }
+    const f32x4 vv = load_in4<BF16>(v, pair * DV + 4 * cg);
+    float bt = beta[pair];
+    raw_t<BF16> kw[L2 ? DK / 64 : 1], qw[L2 ? DK / 64 : 1];  // whole k and q rows for the norms
+    if constexpr (L2) {
+#pragma unroll
+        for (int j = 0; j < DK / 64; ++j) {
+            kw[j] = load_raw<BF16>(k, pair * DK + lane + 64 * j);
+            qw[j] = load_raw<BF16>(q, pair * DK + lane + 64 * j);
+        }
+    }
+    asm volatile("" ::: "memory");  // keep them ahead of the state loads
+    __builtin_amdgcn_sched_barrier(0);
+
+    // 2. stream the thread's state slab in (all loads in flight at once)
+    f32x4 s[RPT];
+#pragma unroll
+    for (int m = 0; m < RPT; ++m)
+        s[m] = __builtin_nontemporal_load(
+            reinterpret_cast<const f32x4*>(S + (int64_t)(rg + m * RG) * DV) + cg);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // while the state is in flight: activations, norms, per-row vectors to LDS
+#pragma unroll
+    for (int j = 0; j < RPS; ++j) {
+        float gj = graw[j];
+        if (front & kFrontGate) gj = -__expf(gj);
+        s_a[t + NT * j] = __expf(gj);
+        s_k[t + NT * j] = in_f32<BF16>(kraw[j]);
+        s_q[t + NT * j] = in_f32<BF16>(qraw[j]);
+    }
+    if (front & kFrontBeta) bt = 1.f / (1.f + __expf(-bt));
+    float kn = 1.f, qn = 1.f;  // inverse norms of k and q (L2)
+    if constexpr (L2) {
+        // No contraction here: a lane's last square fused into the first
+        // exchange's addition would be unrounded in that lane only, and the
+        // lanes (so the row groups and slices) would get different norms.
+#pragma clang fp contract(off)
+        float sk = 0.f, sq = 0.f;
+#pragma unroll
+        for (int j = 0; j < DK / 64; ++j) {
+            const float kx = in_f32<BF16>(kw[j]), qx = in_f32<BF16>(qw[j]);
+            sk = j == 0 ? kx * kx : fmaf(kx, kx, sk);
+            sq = j == 0 ? qx * qx : fmaf(qx, qx, sq);
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+            sk += __shfl_xor(sk, off);
+            sq += __shfl_xor(sq, off);
+        }
+        kn = 1.f / sqrtf(sk + kL2Eps);
+        qn = 1.f / sqrtf(sq + kL2Eps);
+    }
+    __syncthreads();
+
+    // 3. decay in registers; partial S'^T k, S'^T q and k.q over this thread's rows
+    f32x4 r = {0.f, 0.f, 0.f, 0.f}, p = {0.f, 0.f, 0.f, 0.f};
+    float kq = 0.f;
+#pragma unroll
+    for (int m = 0; m < RPT; ++m) {
+        const int i = rg + m * RG;
+        const float ai = s_a[i], ki = s_k[i] * kn, qi = s_q[i] * qn;
+        s[m] *= ai;
+        r += s[m] * ki;
+        p += s[m] * qi;
+        kq += ki * qi;
+    }
+
+    // 4. butterfly over each run of RGW row groups (lanes CGS apart)
+#pragma unroll
+    for (int j = 1; j < RGW; j <<= 1) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            r[e] += __shfl_xor(r[e], CGS * j);
+            p[e] += __shfl_xor(p[e], CGS * j);
+        }
+        kq += __shfl_xor(kq, CGS * j);
+    }
+    if (rg % RGW == 0) {
+        s_red[rg / RGW][cgl][0] = r;
+        s_red[rg / RGW][cgl][1] = p;
+        if (cgl == 0) s_kq[rg / RGW] = kq;
+    }
+    __syncthreads();
+
+    // 5. run sums in ascending order, then the delta-rule correction u
+    f32x4 rr = s_red[0][cgl][0], pp = s_red[0][cgl][1];
+    float kqt = s_kq[0];
+#pragma unroll
+    for (int w = 1; w < NRUN; ++w) {
+        rr += s_red[w][cgl][0];
+        pp += s_red[w][cgl][1];
+        kqt += s_kq[w];
+    }
+    // (every key row belongs to exactly one row group, so kqt = k . q)
+    const f32x4 u = bt * (vv - rr);
+    if (rg == 0) {
+        const f32x4 out = pp + kqt * u;
+        *reinterpret_cast<f32x4*>(o + pair * DV + 4 * cg) = out;
+    }
+
+    // 6. rank-1 write and stream the slab back out
+#pragma unroll
+    for (int m = 0; m < RPT; ++m) {
+        const int i = rg + m * RG;
+        const f32x4 nv = s[m] + (s_k[i] * kn) * u;
+        __builtin_nontemporal_store(nv, reinterpret_cast<f32x4*>(S + (int64_t)i * DV) + cg);
+    }
+}
+
 // Dynamic LDS (never touched by the kernel) that leaves room for only
-// n = max(1, 64 KiB / state bytes) decode workgroups per CU: each asks for
-// lds_per_cu / (n + 1/2) bytes in all, more than a share of n + 1 and no
+// n = max(1, 64 KiB / slice state bytes) decode workgroups per CU: each asks
+// for lds_per_cu / (n + 1/2) bytes in all, more than a share of n + 1 and no
 // more than a share of n.
-template <int DK, int DV>
+template <int DK, int DV, int NS>
 unsigned residency_pad() {
-    constexpr int CG = DV / 4;
-    constexpr int kStatic = 3 * kThreads * 4 + kWaves * CG * 2 * 16 + kWaves * 4;
-    const int n = (DK * DV * 4 >= 65536) ? 1 : 65536 / (DK * DV * 4);
+    constexpr int NT = kThreads / NS, CGS = DV / 4 / NS;
+    constexpr int RPS = (DK + NT - 1) / NT;
+    constexpr int kStatic = 3 * RPS * NT * 4 + kWaves * CGS * 2 * 16 + kWaves * 4;
+    constexpr int kSlice = DK * DV * 4 / NS;
+    const int n = (kSlice >= 65536) ? 1 : 65536 / kSlice;
     const DeviceInfo di = device_info();
     if (!di.valid || di.lds_per_cu <= 0) return 0;
     const int lds = di.lds_per_cu, per_block = di.lds_per_block;
@@ -234,17 +404,39 @@ unsigned residency_pad() {
     return (unsigned)want;
 }
 
+template <int DK, int DV, int NS>
+hipError_t launch_slices(const void* q, const void* k, const void* v, bool bf16, const float* g,
+                         const float* beta, int B, int H, float* state, float* o, unsigned front,
+                         hipStream_t stream) {
+    const dim3 grid((unsigned)((int64_t)B * H * NS)), block(kThreads / NS);
+    const unsigned pad = residency_pad<DK, DV, NS>();
+    const bool l2 = (front & kFrontL2) != 0;
+    void (*kern)(const void*, const void*, const void*, const float*, const float*, float*, float*, unsigned);
+    if constexpr (NS == 1)
+        kern = bf16 ? (l2 ? &decode_kernel<DK, DV, true, true> : &decode_kernel<DK, DV, true, false>)
+                    : (l2 ? &decode_kernel<DK, DV, false, true> : &decode_kernel<DK, DV, false, false>);
+    else
+        kern = bf16 ? (l2 ? &decode_slices_kernel<DK, DV, NS, true, true> : &decode_slices_kernel<DK, DV, NS, true, false>)
+                    : (l2 ? &decode_slices_kernel<DK, DV, NS, false, true> : &decode_slices_kernel<DK, DV, NS, false, false>);
+    hipLaunchKernelGGL(kern, grid, block, pad, stream, q, k, v, g, beta, state, o, front);
+    return hipGetLastError();
+}
+
+// Slices per (b, h), from kernel-trace times on MI355X (D = 128, bf16,
+// H = 32, 256 CUs), with 1 / 2 / 4 slices: B = 1: 4.24 / 3.68 / 3.48 us;
+// B = 4: 5.36 / 4.72 / 4.68; B = 8: 6.48 / 5.64 / 5.64; B = 32: 24.7 / 23.2 /
+// 23.5; B = 64: 47.8 / 46.1 / 47.3; B = 128: 90.4 / 90.8 / 93.5; B = 512:
+// 350 / 380 / 383. So four slices while the pairs cover at most half the
+// CUs, two up to 8 pairs per CU, else one.
 template <int DK, int DV>
 hipError_t launch_dims(const void* q, const void* k, const void* v, bool bf16, const float* g,
                        const float* beta, int B, int H, float* state, float* o, unsigned front,
                        hipStream_t stream) {
-    const dim3 grid((unsigned)((int64_t)B * H)), block(kThreads);
-    const unsigned pad = residency_pad<DK, DV>();
-    const bool l2 = (front & kFrontL2) != 0;
-    auto kern = bf16 ? (l2 ? &decode_kernel<DK, DV, true, true> : &decode_kernel<DK, DV, true, false>)
-                     : (l2 ? &decode_kernel<DK, DV, false, true> : &decode_kernel<DK, DV, false, false>);
-    hipLaunchKernelGGL(kern, grid, block, pad, stream, q, k, v, g, beta, state, o, front);
-    return hipGetLastError();
+    const int64_t pairs = (int64_t)B * H;
+    const int64_t cus = device_info().cus;
+    if (2 * pairs <= cus) return launch_slices<DK, DV, 4>(q, k, v, bf16, g, beta, B, H, state, o, front, stream);
+    if (pairs <= 8 * cus) return launch_slices<DK, DV, 2>(q, k, v, bf16, g, beta, B, H, state, o, front, stream);
+    return launch_slices<DK, DV, 1>(q, k, v, bf16, g, beta, B, H, state, o, front, stream);
 }
 
 // ------------------------------------------------- position advance ----

@@ -84,3 +84,30 @@ def test_decode_deterministic_and_in_place():
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(s1, s2)
     assert not torch.equal(s1, s0)
+
+
+@pytest.mark.parametrize("front", [0, 7])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("Dk,Dv", [(128, 128), (64, 64), (128, 64), (64, 128)])
+def test_decode_batch_invariant(Dk, Dv, dtype, front):
+    """With fewer (b, h) pairs than 8 per CU the step splits each state's
+    value columns over 2 or 4 workgroups, keeping the order of every
+    reduction: a batch row's output and new state are bitwise the same in
+    batches of 1 to 16 rows (four and two slices) as in a batch of 136 rows
+    (4352 pairs, one workgroup each)."""
+    import torch
+    import linear_attention_05_amd as K
+    H, Bbig = 32, 136
+    print(f"decode batch invariance Dk={Dk} Dv={Dv} {dtype} front={front}", flush=True)
+    s0 = decode_state(Bbig, H, Dk, Dv, 61)
+    x = decode_step_inputs(Bbig, H, Dk, Dv, dtype, 61, 0)
+    big = [dev_tensor(a) for a in (x.q, x.k, x.v, x.g, x.beta)]
+    sb = dev_tensor(s0)
+    ob = K.kda_decode_step(*big, sb, frontend=front)
+    for b in (1, 2, 4, 8, 16):
+        ss = dev_tensor(np.ascontiguousarray(s0[:b]))
+        small = [dev_tensor(np.ascontiguousarray(a[:b])) for a in (x.q, x.k, x.v, x.g, x.beta)]
+        os_ = K.kda_decode_step(*small, ss, frontend=front)
+        torch.cuda.synchronize()
+        assert torch.equal(os_, ob[:b]), f"o differs at batch {b}"
+        assert torch.equal(ss, sb[:b]), f"state differs at batch {b}"
