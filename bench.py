@@ -183,6 +183,47 @@ def bench_decode(steps, warmup):
                 bytes=byts, flops=Bsz * H * acc.decode_flops_per_head_token(D, D))
 
 
+def bench_decode_small(batches=(1, 8, 32), steps=32, replays=20):
+    """Decode steps for small batches (H = 32, D = 128, bf16), launched from a
+    captured graph of `steps` steps so that the host's per-call cost (about
+    15 us from Python) does not hide the kernels: us per step over `replays`
+    replays, each step on the state the previous one left."""
+    import torch
+    import linear_attention_05_amd as K
+    from synth import decode_state, decode_step_inputs
+
+    H, D = 32, 128
+    rows = []
+    for Bsz in batches:
+        state = dev(decode_state(Bsz, H, D, D, 71))
+        s = decode_step_inputs(Bsz, H, D, D, "bf16", 71, 0)
+        inp = tuple(dev(a) for a in (s.q, s.k, s.v, s.g, s.beta))
+        o = torch.empty(Bsz, H, D, device="cuda")
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):  # warm-up off the default stream, as capture wants
+            for _ in range(3):
+                K.kda_decode_step(*inp, state, o)
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(steps):
+                K.kda_decode_step(*inp, state, o)
+        graph.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(replays):
+            graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (replays * steps)
+        rows.append({"B": Bsz, "us_per_step": round(us, 2),
+                     "state_gbps": round(Bsz * H * D * D * 8 / (us * 1e3), 1)})
+    return {"workload": "KDA decode H=32 D=128 bf16, steps launched from a captured graph",
+            "batches": rows}
+
+
 def cpu_baseline(x, target_s=10.0):
     """fp64 oracle (all value columns of a growing set of heads, all tokens),
     timed until about target_s seconds of CPU work; reports the median
@@ -617,6 +658,7 @@ def main():
     if args.only == "all" and not args.no_extra_workloads:
         out["frontend"] = bench_frontend()
         out["positions"] = bench_positions()
+        out["decode_small_batches"] = bench_decode_small()
         out["hbm_ceilings"] = hbm_ceilings()
     if args.only in ("all", "prefill") and not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(p["inputs"])
