@@ -359,7 +359,7 @@ def bench_prefill_workload(idx, reps=3):
                 path_roofline_frac=round(byts / (ms * 1e-3) / 8e12, 4))
 
 
-def bench_frontend(steps=10, warmup=3, decode_steps=32):
+def bench_frontend(steps=10, warmup=50, decode_steps=32):
     """The in-kernel parameter-free front-end (KDA_FRONT_*: q/k L2 normalisation,
     g = -exp(u), sigmoid write strength) on raw inputs of the headline prefill
     and decode shapes, beside what the same transforms cost as separate torch
@@ -451,7 +451,7 @@ def bench_frontend(steps=10, warmup=3, decode_steps=32):
         decode_plain_us_per_step=round(dec_plain * 1e3, 2))
 
 
-def bench_positions(reps=10, warmup=3):
+def bench_positions(reps=10, warmup=50):
     """States at arbitrary positions (kda_prefill_chunked_at) on the headline
     prefill: whole calls with four mid-chunk positions, interleaved with plain
     calls on the same inputs."""
