@@ -322,6 +322,11 @@ kda_status_t kda_prefill_chunked_noalloc(
  *   o      [B, H, Dv] fp32
  *   Dk, Dv in {64, 128}; B, H >= 1 (B == 0 is a valid no-op).
  *
+ * Each (b, h)'s output and new state are bitwise the same whatever B and H
+ * (the work is split differently for small batches, with every sum in the
+ * same order), and the call enqueues kernels only, so it may be captured in
+ * a HIP graph.
+ *
  * Returns KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED or KDA_ERR_HIP.
  */
 kda_status_t kda_decode_step(
