@@ -26,7 +26,8 @@
  *     library holds on each device instead.
  *   - All work is enqueued asynchronously on `stream` (0 = the null stream);
  *     no entry point synchronises. Results are visible after the caller
- *     synchronises the stream.
+ *     synchronises the stream. Only kernels are enqueued (no allocation,
+ *     memset or copy), so calls may be captured in a HIP graph.
  *   - Layouts are dense row-major (C order) with the last index contiguous:
  *       q, k  [tokens, H, Dk]     v, o  [tokens, H, Dv]
  *       g     [tokens, H, Dk]     beta  [tokens, H]
