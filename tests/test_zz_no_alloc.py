@@ -87,3 +87,48 @@ def test_noalloc_refuses_more_than_its_scratch():
     st = B.prefill_noalloc_raw(1 << 20, 1 << 20, 1 << 20, B.KDA_BF16, 1 << 20, 1 << 20, None, 1,
                                4032, 32, 128, 128, 64, None, 1 << 20, 0, None, 0, 1 << 20, None)
     assert st == B.KDA_ERR_WORKSPACE
+
+
+def test_noalloc_in_a_graph():
+    """The entry point for callers that cannot allocate, captured in a HIP
+    graph (its first call on the device, which looks up the scratch array's
+    address, runs before the capture) and replayed three times with eager
+    work between the replays: every replay bitwise equal to the eager call."""
+    import torch
+    from linear_attention_05_amd import _binding as B
+    x = make_prefill([300, 129, 700], 4, 128, 128, "bf16", 964, init_state=True)
+    print(f"noalloc in a graph: lengths={x.lengths} H={x.H}", flush=True)
+    q, k, v, g, beta = (dev_tensor(a) for a in (x.q, x.k, x.v, x.g, x.beta))
+    cu = dev_tensor(x.cu_seqlens)
+    s0 = dev_tensor(x.initial_state)
+
+    def call(o, fs):
+        st = B.prefill_noalloc_raw(_ptr(q), _ptr(k), _ptr(v), B.KDA_BF16, _ptr(g), _ptr(beta),
+                                   _ptr(cu), x.num_seqs, x.total_tokens, x.H, x.Dk, x.Dv, 64,
+                                   _ptr(s0), _ptr(fs), 0, None, 0, _ptr(o),
+                                   torch.cuda.current_stream().cuda_stream)
+        assert st == B.KDA_OK, B.status_string(st)
+
+    o_e = torch.empty(x.total_tokens, x.H, x.Dv, device="cuda")
+    fs_e = torch.empty(x.num_seqs, x.H, x.Dk, x.Dv, device="cuda")
+    call(o_e, fs_e)
+    torch.cuda.synchronize()
+    o_g, fs_g = torch.empty_like(o_e), torch.empty_like(fs_e)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(o_g, fs_g)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call(o_g, fs_g)
+    for rep in range(3):
+        o_g.zero_()
+        fs_g.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o_g, o_e), f"replay {rep}: o"
+        assert torch.equal(fs_g, fs_e), f"replay {rep}: final state"
+        call(o_e, fs_e)  # eager work between replays (same results)
+        torch.cuda.synchronize()
