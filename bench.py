@@ -183,6 +183,50 @@ def bench_decode(steps, warmup):
                 bytes=byts, flops=Bsz * H * acc.decode_flops_per_head_token(D, D))
 
 
+def bench_strong_decay(counts=(8, 128), steps=20, warmup=50):
+    """The headline prefill with n channels per head (the same for every
+    head) decaying by -U(0.6, 2) nats per token and the rest by the workload
+    recipe: diagonal 16-token blocks then take the vector-unit form (up to 16
+    such channels) or the four-level products (more)."""
+    import numpy as np
+    import torch
+    import linear_attention_05_amd as K
+    from synth import make_workload
+
+    x = make_workload(PREFILL_WORKLOAD)
+    N, H, D = x.total_tokens, x.H, x.Dk
+    q, k, v, beta, s0 = (dev(a) for a in (x.q, x.k, x.v, x.beta, x.initial_state))
+    o = torch.empty(N, H, D, device="cuda")
+    fs = torch.empty(1, H, D, D, device="cuda")
+    ws = torch.empty(K.kda_prefill_workspace_size(N, 1, H, D, D), dtype=torch.uint8, device="cuda")
+    rng = np.random.default_rng(77)
+    rows = []
+    for n in counts:
+        g = x.g.copy()
+        ch = rng.choice(D, size=n, replace=False)
+        g[:, :, ch] = -rng.uniform(0.6, 2.0, size=(N, H, n)).astype(np.float32)
+        gd = dev(np.ascontiguousarray(g))
+
+        def call():
+            K.kda_prefill_chunked(q, k, v, gd, beta, initial_state=s0, final_state=fs, o=o,
+                                  workspace=ws)
+
+        for _ in range(warmup):
+            call()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            call()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        rows.append({"fast_channels_per_head": n, "ms": round(ms, 4),
+                     "mtok_s": round(N / (ms * 1e-3) / 1e6, 3)})
+    return {"workload": f"prefill B=1 T={N} H={H} D={D} bf16, n channels per head with "
+                        "g = -U(0.6, 2) per token", "runs": rows}
+
+
 def bench_decode_small(batches=(1, 8, 32), steps=32, replays=20):
     """Decode steps for small batches (H = 32, D = 128, bf16), launched from a
     captured graph of `steps` steps so that the host's per-call cost (about
@@ -659,6 +703,7 @@ def main():
         out["frontend"] = bench_frontend()
         out["positions"] = bench_positions()
         out["decode_small_batches"] = bench_decode_small()
+        out["strong_decay"] = bench_strong_decay()
         out["hbm_ceilings"] = hbm_ceilings()
     if args.only in ("all", "prefill") and not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(p["inputs"])
