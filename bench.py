@@ -581,7 +581,8 @@ def main():
     # calls at the headline shape): the default warm-up covers that
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--decode-steps", type=int, default=64)
-    ap.add_argument("--only", choices=["all", "prefill", "decode", "few_heads", "long_varlen"],
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "few_heads", "long_varlen",
+                                       "decode_small", "strong_decay"],
                     default="all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra-workloads", action="store_true",
@@ -633,6 +634,12 @@ def main():
         return
     if args.only == "few_heads":
         out["few_heads"] = [bench_few_heads(4), bench_few_heads(1)]
+        out["kernel_source_sha"] = kernel_source_sha()
+        print(json.dumps(out), flush=True)
+        return
+    if args.only in ("decode_small", "strong_decay"):
+        out["decode_small_batches" if args.only == "decode_small" else args.only] = (
+            bench_decode_small() if args.only == "decode_small" else bench_strong_decay())
         out["kernel_source_sha"] = kernel_source_sha()
         print(json.dumps(out), flush=True)
         return
