@@ -183,7 +183,7 @@ def bench_decode(steps, warmup):
                 bytes=byts, flops=Bsz * H * acc.decode_flops_per_head_token(D, D))
 
 
-def bench_strong_decay(counts=(8, 128), steps=20, warmup=50):
+def bench_strong_decay(counts=(0, 8, 128), steps=20, warmup=50):
     """The headline prefill with n channels per head (the same for every
     head) decaying by -U(0.6, 2) nats per token and the rest by the workload
     recipe: diagonal 16-token blocks then take the vector-unit form (up to 16
