@@ -295,7 +295,7 @@ kda_status_t kda_prefill_chunked_at(
  * never allocated or freed by this call). Sizes whose
  * kda_prefill_workspace_size-style need exceeds it are refused with
  * KDA_ERR_WORKSPACE before any launch: with bf16 q/k/v, H = 32 and
- * Dk = Dv = 128 that allows one sequence of up to 3,968 tokens. Every call on
+ * Dk = Dv = 128 that allows one sequence of up to 4,224 tokens. Every call on
  * a device shares that device's array: calls that overlap in time on one
  * device (different streams or threads) race and give undefined results. The
  * array keeps the last call's contents, which no later call reads. Other

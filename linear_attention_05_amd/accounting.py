@@ -47,9 +47,10 @@ def prefill_compulsory_bytes(n_tok: int, H: int, Dk: int, Dv: int, in_bytes: int
 
 
 def handoff_bytes_per_chunk_head(Dk: int, op_bytes: int) -> int:
-    """K1 -> K2 handoff block: -W, Qd, Kc^T (64*Dk each), P and Ainv*diag(beta)
-    (64*64 each) in the MFMA operand type, plus Gamma_last (Dk fp32)."""
-    return (192 * Dk + 8192) * op_bytes + 4 * Dk
+    """K1 -> K2 handoff block: -W, Qd, Kc^T (64*Dk each), the lower-triangular
+    P and Ainv*diag(beta) (the six of eight 16x32 frags of each 64x64 matrix
+    that hold entries) in the MFMA operand type, plus Gamma_last (Dk fp32)."""
+    return (192 * Dk + 6144) * op_bytes + 4 * Dk
 
 
 def k1_bytes(n_tok: int, H: int, Dk: int, in_bytes: int, op_bytes: int, n_chunks: int) -> int:

@@ -160,8 +160,12 @@ struct Handoff {
     static constexpr size_t kQd = kW + 4 * NKS * 512;
     static constexpr size_t kKc = kQd + 4 * NKS * 512;
     static constexpr size_t kP = kKc + NRT * 2 * 512;
-    static constexpr size_t kAb = kP + 4 * 2 * 512;
-    static constexpr size_t kElems = kAb + 4 * 2 * 512;
+    // P and Ab are lower triangular over the chunk's tokens: of their
+    // (row tile, token slab) frags only the six that hold entries are stored,
+    // (0,0) (1,0) (2,0) (2,1) (3,0) (3,1) in that order
+    static constexpr size_t kAb = kP + 6 * 512;
+    static constexpr size_t kElems = kAb + 6 * 512;
+    static __host__ __device__ constexpr int tri(int rt, int ts) { return rt < 2 ? rt : 2 * rt - 2 + ts; }
     static constexpr size_t kGlastBytes = kElems * sizeof(E);
     static constexpr size_t kBytes = kGlastBytes + DK * sizeof(float);
     static_assert(kBytes % 256 == 0, "handoff block must keep 256-byte alignment");
@@ -787,7 +791,7 @@ __global__ __launch_bounds__(kThreads, BF16 ? 3 : (DK == 128 ? 1 : 2)) void k1_p
                 const int ss = 16 * sb + 4 * q + i, rr = 16 * rb + m;
                 pv[i] = (E)(ss <= rr ? accP[i] : 0.f);
             }
-            *reinterpret_cast<e4*>(hb + HO::kP + ((size_t)(rb * 2 + sb / 2) * 64 + lane) * 8 + 4 * (sb % 2)) = pv;
+            *reinterpret_cast<e4*>(hb + HO::kP + ((size_t)HO::tri(rb, sb / 2) * 64 + lane) * 8 + 4 * (sb % 2)) = pv;
             return at;
         };
         // Qd A-frags (first, so that the prefetched queries die early): rows tokens (tile rt), K channels (slab ks, permuted)
@@ -1007,7 +1011,7 @@ __global__ __launch_bounds__(kThreads, BF16 ? 3 : (DK == 128 ? 1 : 2)) void k1_p
         if (wave == 2 || wave == 3) {
             const int rb = wave == 2 ? 0 : 2, sb = rb + 1;
             typedef E e4 __attribute__((ext_vector_type(4)));
-            *reinterpret_cast<e4*>(hb + HO::kP + ((size_t)(rb * 2 + sb / 2) * 64 + lane) * 8 + 4 * (sb % 2)) = e4{};
+            *reinterpret_cast<e4*>(hb + HO::kP + ((size_t)HO::tri(rb, sb / 2) * 64 + lane) * 8 + 4 * (sb % 2)) = e4{};
         }
         // The slabs (row tiles 0-1, token slab 1) of P and Ab lie wholly
         // above the diagonal: they are zero, and neither stored nor read.
@@ -1173,7 +1177,7 @@ __global__ __launch_bounds__(kThreads, BF16 ? 3 : (DK == 128 ? 1 : 2)) void k1_p
         }
     }
     // Ab = Ainv diag(beta) A-frags: rows tokens (tile rt), K tokens (slab ts, permuted);
-    // slabs (rt 0-1, ts 1) are identically zero (written in phase A).
+    // slabs (rt 0-1, ts 1) are identically zero and not stored.
     {
         // frags (rt, ts): (0,0) (1,0) (2,0) (2,1) (3,0) (3,1)
         for (int f = wave; f < 6; f += 4) {
@@ -1185,7 +1189,7 @@ __global__ __launch_bounds__(kThreads, BF16 ? 3 : (DK == 128 ? 1 : 2)) void k1_p
                 const int s = 32 * ts + perm32(q, e);
                 out[e] = (E)(sA[r][s] * sB[s]);
             }
-            store_frag<Frag, E>(hb + HO::kAb, rt * 2 + ts, lane, out);
+            store_frag<Frag, E>(hb + HO::kAb, f, lane, out);  // f = HO::tri(rt, ts)
         }
     }
 }
@@ -1277,11 +1281,11 @@ __global__ __launch_bounds__(kThreads) void k2_scan_kernel(
     auto load_ops = [&](Ops& op, int n, int grp) {
         const E* hb = reinterpret_cast<const E*>(hbase + (size_t)n * HO::kBytes);
         if (grp == 0) {
-            op.ab[0] = load_frag<Frag, E>(hb + HO::kAb, rt * 2, lane);
-            op.p[0] = load_frag<Frag, E>(hb + HO::kP, rt * 2, lane);
+            op.ab[0] = load_frag<Frag, E>(hb + HO::kAb, HO::tri(rt, 0), lane);
+            op.p[0] = load_frag<Frag, E>(hb + HO::kP, HO::tri(rt, 0), lane);
             if (rt >= 2) {  // token slab 1 of row tiles 0-1 is zero (not stored)
-                op.ab[1] = load_frag<Frag, E>(hb + HO::kAb, rt * 2 + 1, lane);
-                op.p[1] = load_frag<Frag, E>(hb + HO::kP, rt * 2 + 1, lane);
+                op.ab[1] = load_frag<Frag, E>(hb + HO::kAb, HO::tri(rt, 1), lane);
+                op.p[1] = load_frag<Frag, E>(hb + HO::kP, HO::tri(rt, 1), lane);
             } else {
                 op.ab[1] = Frag{};
                 op.p[1] = Frag{};
@@ -1735,8 +1739,8 @@ __global__ __launch_bounds__(192) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             const E* hb = hptr(n);
 #pragma unroll
             for (int r = 0; r < NRT; ++r) {
-                ab0[r] = load_frag<Frag, E>(hb + HO::kAb, r * 2, lane);
-                if (r >= 2) ab1[r - 2] = load_frag<Frag, E>(hb + HO::kAb, r * 2 + 1, lane);
+                ab0[r] = load_frag<Frag, E>(hb + HO::kAb, HO::tri(r, 0), lane);
+                if (r >= 2) ab1[r - 2] = load_frag<Frag, E>(hb + HO::kAb, HO::tri(r, 1), lane);
             }
             gr = *reinterpret_cast<const f32x4*>(
                 reinterpret_cast<const float*>(reinterpret_cast<const unsigned char*>(hb) + HO::kGlastBytes) +
@@ -1844,9 +1848,9 @@ __global__ __launch_bounds__(192) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
                 for (int r = 0; r < NRT; ++r) qd[r][ks] = load_frag<Frag, E>(hb + HO::kQd, r * NKS + ks, lane);
 #pragma unroll
-            for (int r = 0; r < NRT; ++r) pp0[r] = load_frag<Frag, E>(hb + HO::kP, r * 2, lane);
-            pp1[0] = load_frag<Frag, E>(hb + HO::kP, 5, lane);
-            pp1[1] = load_frag<Frag, E>(hb + HO::kP, 7, lane);
+            for (int r = 0; r < NRT; ++r) pp0[r] = load_frag<Frag, E>(hb + HO::kP, HO::tri(r, 0), lane);
+            pp1[0] = load_frag<Frag, E>(hb + HO::kP, HO::tri(2, 1), lane);
+            pp1[1] = load_frag<Frag, E>(hb + HO::kP, HO::tri(3, 1), lane);
         };
         // O(n)^T from the fragments wave 0 left at parity n & 1; lane (q, m)
         // holds token 16 r + m, columns 4q .. 4q+3. n = -1 is a dry run whose
@@ -2207,8 +2211,8 @@ __global__ __launch_bounds__(64 * (NCB + 3)) __attribute__((amdgpu_waves_per_eu(
             const E* hb = hptr(n);
 #pragma unroll
             for (int r = 0; r < NRT; ++r) {
-                ab0[r] = load_frag<Frag, E>(hb + HO::kAb, r * 2, lane);
-                if (r >= 2) ab1[r - 2] = load_frag<Frag, E>(hb + HO::kAb, r * 2 + 1, lane);
+                ab0[r] = load_frag<Frag, E>(hb + HO::kAb, HO::tri(r, 0), lane);
+                if (r >= 2) ab1[r - 2] = load_frag<Frag, E>(hb + HO::kAb, HO::tri(r, 1), lane);
             }
             gr = *reinterpret_cast<const f32x4*>(
                 reinterpret_cast<const float*>(reinterpret_cast<const unsigned char*>(hb) + HO::kGlastBytes) +
@@ -2281,9 +2285,9 @@ __global__ __launch_bounds__(64 * (NCB + 3)) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
                 for (int r = 0; r < NRT; ++r) qd[r][ks] = load_frag<Frag, E>(hb + HO::kQd, r * NKS + ks, lane);
 #pragma unroll
-            for (int r = 0; r < NRT; ++r) pp0[r] = load_frag<Frag, E>(hb + HO::kP, r * 2, lane);
-            pp1[0] = load_frag<Frag, E>(hb + HO::kP, 5, lane);
-            pp1[1] = load_frag<Frag, E>(hb + HO::kP, 7, lane);
+            for (int r = 0; r < NRT; ++r) pp0[r] = load_frag<Frag, E>(hb + HO::kP, HO::tri(r, 0), lane);
+            pp1[0] = load_frag<Frag, E>(hb + HO::kP, HO::tri(2, 1), lane);
+            pp1[1] = load_frag<Frag, E>(hb + HO::kP, HO::tri(3, 1), lane);
         };
         // O(n)^T of both blocks from the fragments the chains left at parity
         // n & 1; lane (q, m) holds token 16 r + m, columns 4q .. 4q+3. n = -1
@@ -2490,7 +2494,7 @@ __global__ __launch_bounds__(kThreads) void advance_chunk_kernel(
     for (int rt = 0; rt < 4; ++rt) {
 #pragma unroll
         for (int ts = 0; ts < 2; ++ts)  // token slab 1 of row tiles 0-1 is zero (not stored)
-            abf[rt][ts] = (ts == 0 || rt >= 2) ? load_frag<Frag, E>(hb + HO::kAb, rt * 2 + ts, lane) : Frag{};
+            abf[rt][ts] = (ts == 0 || rt >= 2) ? load_frag<Frag, E>(hb + HO::kAb, HO::tri(rt, ts), lane) : Frag{};
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) wnf[rt][ks] = load_frag<Frag, E>(hb + HO::kW, rt * NKS + ks, lane);
     }

@@ -45,11 +45,11 @@ def ws_size(N=8192, S=1, H=32, Dk=128, Dv=128, chunk=64, dt=B.KDA_BF16):
 
 
 def test_workspace_size():
-    per_chunk_bf16 = (192 * 128 + 8192) * 2 + 4 * 128
-    assert per_chunk_bf16 == 66048
+    per_chunk_bf16 = (192 * 128 + 6144) * 2 + 4 * 128
+    assert per_chunk_bf16 == 61952
     table = 256 + 64 * 256 * 8 * 4  # sequence tables + store sink
     assert ws_size() == table + 32 * (8192 // 64 + 1) * per_chunk_bf16
-    per_chunk_f32 = (192 * 64 + 8192) * 4 + 4 * 64
+    per_chunk_f32 = (192 * 64 + 6144) * 4 + 4 * 64
     assert ws_size(256, 1, 2, 64, 64, 64, B.KDA_F32) == table + 2 * 5 * per_chunk_f32
     assert ws_size(Dk=96) == 0
     assert ws_size(chunk=32) == 0
@@ -208,7 +208,7 @@ def prefill_noalloc(**kw):
     (dict(q=None), INV), (dict(o=None), INV), (dict(N=-1), INV), (dict(Dk=96), UNS),
     (dict(S=2), INV), (dict(ci=96), UNS), (dict(v=A + 2), INV),
     # more scratch than the library's fixed 128 MiB: refused, nothing launched
-    (dict(N=4032, H=32), WS), (dict(N=1 << 20, H=32), WS),
+    (dict(N=4288, H=32), WS), (dict(N=1 << 20, H=32), WS),
 ])
 def test_prefill_noalloc_validation(kw, status):
     """Every refusal happens before any HIP call (these run without a GPU)."""
@@ -216,6 +216,6 @@ def test_prefill_noalloc_validation(kw, status):
 
 
 def test_noalloc_limit_is_the_stated_one():
-    """The stated limit: one sequence of 3,968 tokens fits at H = 32, D = 128,
-    bf16 (its workspace need is at most 128 MiB); 4,032 does not."""
-    assert ws_size(N=3968) <= 128 << 20 < ws_size(N=4032)
+    """The stated limit: one sequence of 4,224 tokens fits at H = 32, D = 128,
+    bf16 (its workspace need is at most 128 MiB); 4,288 does not."""
+    assert ws_size(N=4224) <= 128 << 20 < ws_size(N=4288)

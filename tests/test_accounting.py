@@ -21,4 +21,4 @@ def test_prefill_flop_convention():
     assert acc.prefill_flops_per_token_head(128, 128) == 180224
     assert acc.io_bytes_per_token_head(128, 128, 2) == 1796
     assert acc.io_bytes_per_token_head(64, 64, 4) == 1284
-    assert acc.handoff_bytes_per_chunk_head(128, 2) == 66048
+    assert acc.handoff_bytes_per_chunk_head(128, 2) == 61952

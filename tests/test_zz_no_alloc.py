@@ -70,9 +70,9 @@ def check(x, what):
 
 
 def test_noalloc_two_calls_second_smaller():
-    # the largest size the scratch holds (one sequence of 3968 tokens, 32 heads,
+    # the largest size the scratch holds (one sequence of 4224 tokens, 32 heads,
     # D = 128, bf16), then a smaller varlen batch with checkpoints
-    check(make_prefill([3968], 32, 128, 128, "bf16", 960, init_state=True), "max size")
+    check(make_prefill([4224], 32, 128, 128, "bf16", 960, init_state=True), "max size")
     check(make_prefill([300, 0, 129, 64], 4, 128, 128, "bf16", 961, init_state=True,
                        ckpt_interval=64), "smaller varlen")
 
@@ -85,7 +85,7 @@ def test_noalloc_fp32_then_smaller():
 def test_noalloc_refuses_more_than_its_scratch():
     from linear_attention_05_amd import _binding as B
     st = B.prefill_noalloc_raw(1 << 20, 1 << 20, 1 << 20, B.KDA_BF16, 1 << 20, 1 << 20, None, 1,
-                               4032, 32, 128, 128, 64, None, 1 << 20, 0, None, 0, 1 << 20, None)
+                               4288, 32, 128, 128, 64, None, 1 << 20, 0, None, 0, 1 << 20, None)
     assert st == B.KDA_ERR_WORKSPACE
 
 
